@@ -1,0 +1,237 @@
+"""Pins for the oracle's NVFP4 activation quantiser, expert FFN and combine (CPU only)."""
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import expit
+
+import oracle
+from synth import WORKLOADS, activations, bf16_bits_from_f32, expert_weights, logits as gen_logits, random_bf16
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    d = {}
+    with open(os.path.join(GOLD, name)) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                k, *v = line.split()
+                d[k] = [float(x) for x in v]
+    return d
+
+
+def _e2m1_table():
+    with open(os.path.join(GOLD, "e2m1_magnitudes.txt")) as f:
+        return [float(v) for line in f if not line.startswith("#") for v in line.split()]
+
+
+def test_unit_scale_saturates_at_page_cap():
+    g = _golden("activation_outliers.txt")
+    cap = g["cap"][0]
+    assert cap == 6 * 448
+    for amax in g["outlier_amax"] + [cap]:
+        x = np.zeros((1, 16), np.float32)
+        x[0, 3] = amax
+        x[0, 9] = -amax
+        x[0, 5] = 1.0
+        codes, scales = oracle.quantize_nvfp4(bf16_bits_from_f32(x), 1.0)
+        assert scales[0, 0] == 0x7E                           # 448
+        v = oracle.dequant_nvfp4_act(codes, scales)
+        assert v[0, 3] == cap and v[0, 9] == -cap
+        assert v[0, 5] == 0.0                                  # 1/448 rounds to 0 in E2M1
+
+
+def test_benign_block_is_fine_grained():
+    g = _golden("activation_outliers.txt")
+    amax = g["benign_amax"][0]
+    x = np.linspace(-amax, amax, 16, dtype=np.float32)[None, :]
+    codes, scales = oracle.quantize_nvfp4(bf16_bits_from_f32(x), 1.0)
+    s = oracle.e4m3_value(scales)[0, 0]
+    assert s == 30.0                                           # E4M3(183/6 = 30.5) = 30 (ties to even)
+
+
+def _brute_block(xs, g):
+    table = _e2m1_table()
+    e4 = [(Fraction(float(v)), b) for b, v in enumerate(oracle.e4m3_value(np.arange(0x7F)))]
+    amax = max(abs(Fraction(float(v))) for v in xs)
+    target = min(amax / (6 * Fraction(g)), Fraction(448))
+    best = min(e4, key=lambda p: (abs(p[0] - target), p[1] % 2))
+    s = best[0]
+    nibs = []
+    for v in xs:
+        fv = Fraction(float(v))
+        if s == 0:
+            nibs.append(0)
+            continue
+        r = min(abs(fv) / (s * Fraction(g)), Fraction(6))
+        mag = min(range(8), key=lambda i: (abs(r - Fraction(table[i])), i % 2))
+        nibs.append(mag | (8 if np.signbit(v) else 0))
+    return best[1], nibs
+
+
+@pytest.mark.parametrize("g", [1.0, 0.5, 4.0])
+def test_quantizer_brute_force(g):
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((8, 64)) * 10.0 ** rng.integers(-3, 3, (8, 1))).astype(np.float32)
+    # exact ties: multiples of a quarter of an E4M3-representable block scale
+    x[0, :16] = np.array([6, 5, 4, 3.5, 3, 2.5, 2, 1.75, 1.5, 1.25, 1, .75, .5, .25, 0, -0.0]) * 3.0
+    x[1, :16] = 0.0
+    x[1, 16:32] = 1e-5                                          # scale rounds to 0
+    x[2, 16:32] = -0.0
+    xb = bf16_bits_from_f32(x)
+    codes, scales = oracle.quantize_nvfp4(xb, g)
+    nib = oracle.unpack_codes(codes)
+    xv = oracle.bf16_value(xb)
+    for r in range(x.shape[0]):
+        for b in range(x.shape[1] // 16):
+            sb, nibs = _brute_block(xv[r, b * 16:(b + 1) * 16], g)
+            assert scales[r, b] == sb, (r, b)
+            assert list(nib[r, b * 16:(b + 1) * 16]) == nibs, (r, b)
+
+
+def test_silu_and_swiglu_closed_form():
+    v = np.linspace(-30, 30, 1001)
+    np.testing.assert_allclose(oracle.silu(v), v * expit(v), rtol=1e-14, atol=1e-300)
+    # one-hot input picks column j of gate and up: z = silu(Wg[:, j]) * Wu[:, j]
+    rng = np.random.default_rng(4)
+    wg, wu, wd = rng.standard_normal((3, 64, 32))
+    j = 7
+    x = np.zeros((1, 32), np.float32)
+    x[0, j] = 1.0
+    z, o = oracle.expert_ffn(bf16_bits_from_f32(x), wg, wu, wd.T.copy())
+    ref = wg[:, j] * expit(wg[:, j]) * wu[:, j]
+    assert np.array_equal(z[0], torch.from_numpy(ref).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)) or \
+        np.allclose(oracle.bf16_value(z[0]), ref, rtol=2 ** -8)
+
+
+def test_gate_up_exact_on_tiny():
+    """Tiny shape: the float64 gate/up pre-activations equal exact rational arithmetic."""
+    w = WORKLOADS["tiny"]
+    x = activations(w, 32)
+    W = expert_weights(w)
+    table = _e2m1_table()
+    for e in range(0, 32, 4):
+        wg = oracle.dequant_mx(W["gate"][0][e], W["gate"][1][e])
+        got = oracle.bf16_value(x[:4]) @ wg.T
+        for t in range(4):
+            xs = [Fraction(float(v)) for v in oracle.bf16_value(x[t])]
+            for n in range(0, w.shape.inter, 37):
+                acc = Fraction(0)
+                for k in range(w.shape.hidden):
+                    byte = int(W["gate"][0][e, n, k // 2])
+                    nib = (byte & 0xF) if k % 2 == 0 else byte >> 4
+                    val = Fraction(table[nib & 7]) * (-1 if nib & 8 else 1) * Fraction(2) ** (int(W["gate"][1][e, n, k // 32]) - 127)
+                    acc += val * xs[k]
+                assert Fraction(float(got[t, n])) == acc
+
+
+def test_combine_linearity():
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal((4, 1, 64))
+    o = np.repeat(v, 8, axis=1)
+    wts = rng.uniform(0.1, 1, (4, 8))
+    wts = wts / wts.sum(1, keepdims=True) * 2.827
+    y = oracle.combine(o, wts)
+    ref = oracle.round_to_bf16_bits(2.827 * v[:, 0, :])
+    # sum of weights is 2.827 up to rounding of the float64 weights
+    assert np.max(np.abs(oracle.bf16_value(y) - oracle.bf16_value(ref))) <= np.max(np.abs(v)) * 2 ** -7
+    res = random_bf16(6, (4, 64))
+    y2 = oracle.combine(np.zeros((4, 8, 64)), wts, res)
+    assert np.array_equal(y2, res)
+
+
+def _independent_tiny_layer(x_bits, l, W, s):
+    """Straight per-token loops with the golden E2M1 table and torch's E8M0 codec."""
+    table = np.array(_e2m1_table())
+
+    def deq(packed, scale):
+        nib = np.stack([packed & 0xF, packed >> 4], -1).reshape(packed.shape[0], -1)
+        val = table[nib & 7] * np.where(nib & 8, -1.0, 1.0)
+        sc = torch.from_numpy(scale.copy()).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+        return val * np.repeat(sc, 32, axis=1)
+
+    x = torch.from_numpy(x_bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    y = np.zeros_like(x)
+    for t in range(x.shape[0]):
+        ids, wts = _brute(l[t], s)
+        for e, wt in zip(ids, wts):
+            g = deq(W["gate"][0][e], W["gate"][1][e]) @ x[t]
+            u = deq(W["up"][0][e], W["up"][1][e]) @ x[t]
+            zf = g * expit(g) * u
+            z = torch.from_numpy(zf).to(torch.bfloat16).to(torch.float64).numpy()
+            y[t] += wt * (deq(W["down"][0][e], W["down"][1][e]) @ z)
+    return y
+
+
+def _brute(lt, s):
+    sg = expit(lt.astype(np.float64))
+    gs = s.num_experts // s.n_group
+    gsc = [np.sort(sg[g * gs:(g + 1) * gs])[-2:].sum() for g in range(s.n_group)]
+    kept = sorted(range(s.n_group), key=lambda g: (-gsc[g], g))[:s.topk_group]
+    cand = sorted([e for g in kept for e in range(g * gs, (g + 1) * gs)], key=lambda e: (-sg[e], e))[:s.top_k]
+    w = sg[cand]
+    return cand, w / w.sum() * s.routed_scaling_factor
+
+
+def test_tiny_layer_against_independent_loops():
+    w = WORKLOADS["tiny"]
+    s = w.shape
+    x = activations(w, 32)
+    l = gen_logits(w, 32)
+    W = expert_weights(w)
+    res = oracle.moe_layer(x, l, None, W, s.n_group, s.topk_group, s.top_k, s.routed_scaling_factor)
+    ref = _independent_tiny_layer(x, l, W, s)
+    got = oracle.bf16_value(res.y)
+    # z goes through a float64->float32->bf16 double rounding in torch above; allow an ulp of z
+    rms = np.sqrt(np.mean(ref ** 2))
+    assert np.max(np.abs(got - ref)) <= 2e-3 * rms + np.max(np.abs(ref)) * 2 ** -8
+
+
+def _fake_quant_brute(v):
+    """NVFP4 quantise-dequantise of float64 values (bf16-exact) with the brute-force rules above."""
+    table = _e2m1_table()
+    out = np.empty_like(v)
+    e4 = oracle.e4m3_value(np.arange(0x7F))
+    for r in range(v.shape[0]):
+        for b in range(v.shape[1] // 16):
+            blk = v[r, b * 16:(b + 1) * 16]
+            sb, nibs = _brute_block(blk, 1.0)
+            out[r, b * 16:(b + 1) * 16] = [table[n & 7] * (-1 if n & 8 else 1) * e4[sb] for n in nibs]
+    return out
+
+
+def test_tiny_w4a4_layer_against_brute_force():
+    """W4A4 on the tiny shape: x and z both fake-quantised by the brute-force rules."""
+    w = WORKLOADS["tiny"]
+    s = w.shape
+    T = 6
+    x = activations(w, 32)[:T]
+    l = gen_logits(w, 32)[:T]
+    W = expert_weights(w)
+    nv = {}
+    for name in ("gate", "up", "down"):
+        sc, g, _ = oracle.transcode_mx_to_nv(W[name][1], W[name][0])
+        nv[name] = (W[name][0], sc, g)
+    res = oracle.moe_layer(x, l, None, nv, s.n_group, s.topk_group, s.top_k, s.routed_scaling_factor,
+                           fmt="nv", act_mode="nvfp4")
+    xq = _fake_quant_brute(oracle.bf16_value(x))
+    y = np.zeros((T, s.hidden))
+    for t in range(T):
+        ids, wts = _brute(l[t], s)
+        for j, (e, wt) in enumerate(zip(ids, wts)):
+            wg = oracle.dequant_mx(W["gate"][0][e], W["gate"][1][e])
+            wu = oracle.dequant_mx(W["up"][0][e], W["up"][1][e])
+            wd = oracle.dequant_mx(W["down"][0][e], W["down"][1][e])
+            g = wg @ xq[t]
+            u = wu @ xq[t]
+            z = oracle.bf16_value(oracle.round_to_bf16_bits(g * expit(g) * u))
+            assert np.array_equal(oracle.round_to_bf16_bits(z), res.z[t, j]) or \
+                np.max(np.abs(z - oracle.bf16_value(res.z[t, j]))) <= np.max(np.abs(z)) * 2 ** -7
+            zq = _fake_quant_brute(oracle.bf16_value(res.z[t, j])[None, :])[0]
+            y[t] += wt * (wd @ zq)
+    got = oracle.bf16_value(res.y)
+    assert np.max(np.abs(got - y)) <= np.max(np.abs(y)) * 2 ** -8
