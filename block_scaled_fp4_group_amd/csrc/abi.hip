@@ -1,0 +1,232 @@
+// C entry points: argument checks on the host, then kernel launches.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "gemm_common.h"
+
+namespace moe {
+
+static thread_local char g_err[512];
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+moe_status launch_status(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("%s: kernel launch failed: %s", what, hipGetErrorString(e));
+    return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+moe_status launch_route(const float*, const float*, int64_t, const moe_route_params*, int32_t*, float*, hipStream_t);
+size_t permute_ws_bytes(int64_t R, int E);
+moe_status launch_permute(const int32_t*, int64_t, int, int, int32_t*, int32_t*, int32_t*, void*, hipStream_t);
+moe_status launch_combine(const void*, const int32_t*, const float*, const void*, int64_t, int, int, void*, hipStream_t);
+moe_status launch_transcode(const uint8_t*, const uint8_t*, int64_t, int, int, uint8_t*, float*, int64_t*, hipStream_t);
+moe_status launch_quant(const void*, int64_t, int, float, uint8_t*, uint8_t*, hipStream_t);
+moe_status launch_gemm_decode(const GemmArgs&, bool swiglu, bool w_nv, bool a_nv, int64_t rows, hipStream_t);
+moe_status launch_gemm_prefill(const GemmArgs&, bool swiglu, bool w_nv, bool a_nv, int64_t rows, hipStream_t);
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static bool is_pow2_float(float g) {
+  if (!(g > 0.0f)) return false;
+  int e;
+  float m = frexpf(g, &e);
+  return m == 0.5f;
+}
+
+#define MOE_CHECK(cond, ...)      \
+  do {                            \
+    if (!(cond)) {                \
+      moe::set_error(__VA_ARGS__); \
+      return MOE_ERR_INVALID;     \
+    }                             \
+  } while (0)
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+const char* moe_version(void) { return "moe_fp4 gfx950 1.0"; }
+
+moe_status moe_route(const float* logits, const float* correction_bias, int64_t T, const moe_route_params* p,
+                     int32_t* topk_ids, float* topk_weights, hipStream_t stream) {
+  g_err[0] = 0;
+  MOE_CHECK(p != nullptr, "moe_route: params is NULL");
+  MOE_CHECK(T >= 0, "moe_route: T < 0");
+  const int E = p->num_experts;
+  MOE_CHECK(E >= 2 && E <= 256, "moe_route: num_experts %d outside [2, 256]", E);
+  MOE_CHECK(p->n_group >= 1 && p->n_group <= 64 && E % p->n_group == 0, "moe_route: bad n_group %d", p->n_group);
+  MOE_CHECK(E / p->n_group >= 2, "moe_route: groups need >= 2 experts");
+  MOE_CHECK(p->topk_group >= 1 && p->topk_group <= p->n_group, "moe_route: bad topk_group %d", p->topk_group);
+  MOE_CHECK(p->top_k >= 1 && p->top_k <= 16 && p->top_k <= p->topk_group * (E / p->n_group),
+            "moe_route: bad top_k %d", p->top_k);
+  if (T == 0) return MOE_OK;
+  MOE_CHECK(logits && topk_ids && topk_weights, "moe_route: NULL pointer");
+  return launch_route(logits, correction_bias, T, p, topk_ids, topk_weights, stream);
+}
+
+size_t moe_permute_workspace_bytes(int64_t T, int32_t top_k, int32_t num_experts) {
+  if (T < 0 || top_k <= 0 || num_experts <= 0) return 0;
+  return permute_ws_bytes(T * top_k, num_experts);
+}
+
+moe_status moe_permute(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t num_experts,
+                       int32_t* expert_offsets, int32_t* sorted_slots, int32_t* slot_rows, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  MOE_CHECK(T >= 0 && top_k >= 1, "moe_permute: bad T / top_k");
+  MOE_CHECK(num_experts >= 1 && num_experts <= 1024, "moe_permute: num_experts %d outside [1, 1024]", num_experts);
+  MOE_CHECK(T * (int64_t)top_k < ((int64_t)1 << 31), "moe_permute: too many slots");
+  MOE_CHECK(expert_offsets != nullptr, "moe_permute: expert_offsets is NULL");
+  if (T > 0) MOE_CHECK(topk_ids && sorted_slots && slot_rows, "moe_permute: NULL pointer");
+  size_t need = permute_ws_bytes(T * top_k, num_experts);
+  if (T * (int64_t)top_k > 2048) {
+    if (workspace_bytes < need || workspace == nullptr) {
+      set_error("moe_permute: workspace %zu bytes < %zu", workspace_bytes, need);
+      return MOE_ERR_WORKSPACE;
+    }
+  }
+  return launch_permute(topk_ids, T, top_k, num_experts, expert_offsets, sorted_slots, slot_rows, workspace, stream);
+}
+
+static moe_status check_weights(const moe_fp4_weights* w, const char* name) {
+  MOE_CHECK(w != nullptr, "moe_fp4_grouped_gemm: %s is NULL", name);
+  MOE_CHECK(w->format == MOE_FP4_MX || w->format == MOE_FP4_NV, "moe_fp4_grouped_gemm: %s bad format", name);
+  MOE_CHECK(w->num_experts >= 1 && w->n >= 16 && w->k >= 128, "moe_fp4_grouped_gemm: %s bad shape", name);
+  MOE_CHECK(w->packed && w->scale, "moe_fp4_grouped_gemm: %s NULL data", name);
+  MOE_CHECK(aligned16(w->packed), "moe_fp4_grouped_gemm: %s codes not 16-byte aligned", name);
+  if (w->format == MOE_FP4_NV) MOE_CHECK(w->global_scale != nullptr, "moe_fp4_grouped_gemm: %s NV without global", name);
+  if (w->k % 128 != 0 || w->n % 16 != 0) {
+    set_error("moe_fp4_grouped_gemm: %s needs k %% 128 == 0 and n %% 16 == 0 (n=%d k=%d)", name, w->n, w->k);
+    return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_fp4_grouped_gemm(const moe_act* a, const moe_fp4_weights* w0, const moe_fp4_weights* w1,
+                                moe_epilogue epi, const int32_t* expert_offsets, int64_t rows, const moe_out* out,
+                                int32_t algo, hipStream_t stream) {
+  g_err[0] = 0;
+  MOE_CHECK(a && out && expert_offsets, "moe_fp4_grouped_gemm: NULL argument");
+  MOE_CHECK(epi == MOE_EPI_NONE || epi == MOE_EPI_SWIGLU, "moe_fp4_grouped_gemm: bad epilogue");
+  moe_status st = check_weights(w0, "w0");
+  if (st) return st;
+  if (epi == MOE_EPI_SWIGLU) {
+    st = check_weights(w1, "w1");
+    if (st) return st;
+    MOE_CHECK(w1->format == w0->format && w1->num_experts == w0->num_experts && w1->n == w0->n && w1->k == w0->k,
+              "moe_fp4_grouped_gemm: w0 / w1 differ");
+  }
+  MOE_CHECK(rows >= 0, "moe_fp4_grouped_gemm: rows < 0");
+  MOE_CHECK(a->mode == MOE_ACT_BF16 || a->mode == MOE_ACT_NVFP4, "moe_fp4_grouped_gemm: bad activation mode");
+  MOE_CHECK(a->data != nullptr && aligned16(a->data), "moe_fp4_grouped_gemm: activation data NULL or unaligned");
+  if (a->mode == MOE_ACT_NVFP4) {
+    MOE_CHECK(a->scales != nullptr, "moe_fp4_grouped_gemm: NVFP4 activations need scales");
+    MOE_CHECK(is_pow2_float(a->input_scale), "moe_fp4_grouped_gemm: input_scale must be a power of two");
+  }
+  if (a->gather) MOE_CHECK(a->gather_div >= 1, "moe_fp4_grouped_gemm: gather_div < 1");
+  MOE_CHECK(out->data || out->codes, "moe_fp4_grouped_gemm: no output");
+  if (out->data) MOE_CHECK(aligned16(out->data), "moe_fp4_grouped_gemm: output not 16-byte aligned");
+  if (out->codes) {
+    MOE_CHECK(out->scales != nullptr, "moe_fp4_grouped_gemm: NVFP4 output needs scales");
+    MOE_CHECK(is_pow2_float(out->output_scale), "moe_fp4_grouped_gemm: output_scale must be a power of two");
+  }
+  MOE_CHECK(algo >= MOE_ALGO_AUTO && algo <= MOE_ALGO_PREFILL, "moe_fp4_grouped_gemm: bad algo");
+  if (rows == 0) return MOE_OK;
+
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.a_data = (const uint8_t*)a->data;
+  g.a_scales = a->scales;
+  g.a_gscale = a->mode == MOE_ACT_NVFP4 ? a->input_scale : 1.0f;
+  g.gather = a->gather;
+  g.gather_div = a->gather ? a->gather_div : 1;
+  g.w_packed[0] = w0->packed;
+  g.w_scale[0] = w0->scale;
+  g.w_global[0] = w0->global_scale;
+  const moe_fp4_weights* wl = epi == MOE_EPI_SWIGLU ? w1 : w0;
+  g.w_packed[1] = wl->packed;
+  g.w_scale[1] = wl->scale;
+  g.w_global[1] = wl->global_scale;
+  g.E = w0->num_experts;
+  g.N = w0->n;
+  g.K = w0->k;
+  g.offsets = expert_offsets;
+  g.rows = rows;
+  g.out_bf16 = (uint16_t*)out->data;
+  g.out_codes = out->codes;
+  g.out_scales = out->scales;
+  g.out_inv_g = out->codes ? 1.0f / out->output_scale : 1.0f;
+
+  const bool swiglu = epi == MOE_EPI_SWIGLU;
+  const bool w_nv = w0->format == MOE_FP4_NV;
+  const bool a_nv = a->mode == MOE_ACT_NVFP4;
+  int use = algo;
+  if (use == MOE_ALGO_AUTO) use = (rows >= 32LL * g.E) ? MOE_ALGO_PREFILL : MOE_ALGO_DECODE;
+  if (use == MOE_ALGO_PREFILL) return launch_gemm_prefill(g, swiglu, w_nv, a_nv, rows, stream);
+  return launch_gemm_decode(g, swiglu, w_nv, a_nv, rows, stream);
+}
+
+moe_status moe_combine(const void* expert_out, const int32_t* slot_rows, const float* topk_weights,
+                       const void* residual, int64_t T, int32_t top_k, int32_t h, void* y, hipStream_t stream) {
+  g_err[0] = 0;
+  MOE_CHECK(T >= 0 && top_k >= 1 && top_k <= 32, "moe_combine: bad T / top_k");
+  MOE_CHECK(h >= 8 && h % 8 == 0, "moe_combine: h %% 8 != 0");
+  if (T == 0) return MOE_OK;
+  MOE_CHECK(expert_out && slot_rows && topk_weights && y, "moe_combine: NULL pointer");
+  MOE_CHECK(aligned16(expert_out) && aligned16(y) && (!residual || aligned16(residual)),
+            "moe_combine: bf16 buffers must be 16-byte aligned");
+  return launch_combine(expert_out, slot_rows, topk_weights, residual, T, top_k, h, y, stream);
+}
+
+moe_status fp4_transcode_mx_to_nv(const uint8_t* mx_scale, const uint8_t* packed, int64_t num_mats, int32_t n,
+                                  int32_t k, uint8_t* nv_scale, float* global_scale, int64_t* counters,
+                                  hipStream_t stream) {
+  g_err[0] = 0;
+  MOE_CHECK(num_mats >= 0 && n >= 1 && k >= 32, "fp4_transcode_mx_to_nv: bad sizes");
+  MOE_CHECK(k % 32 == 0 && n % 16 == 0, "fp4_transcode_mx_to_nv: needs k %% 32 == 0 and n %% 16 == 0");
+  MOE_CHECK(counters != nullptr, "fp4_transcode_mx_to_nv: counters is NULL");
+  if (num_mats > 0) {
+    MOE_CHECK(mx_scale && packed && nv_scale && global_scale, "fp4_transcode_mx_to_nv: NULL pointer");
+    MOE_CHECK(aligned16(mx_scale) && aligned16(packed) && aligned16(nv_scale),
+              "fp4_transcode_mx_to_nv: buffers must be 16-byte aligned");
+  }
+  return launch_transcode(mx_scale, packed, num_mats, n, k, nv_scale, global_scale, counters, stream);
+}
+
+moe_status moe_quantize_nvfp4(const void* x, int64_t rows, int32_t k, float input_scale, uint8_t* codes,
+                              uint8_t* scales, hipStream_t stream) {
+  g_err[0] = 0;
+  MOE_CHECK(rows >= 0 && k >= 32 && k % 32 == 0, "moe_quantize_nvfp4: needs k %% 32 == 0");
+  MOE_CHECK(is_pow2_float(input_scale), "moe_quantize_nvfp4: input_scale must be a power of two");
+  if (rows == 0) return MOE_OK;
+  MOE_CHECK(x && codes && scales, "moe_quantize_nvfp4: NULL pointer");
+  MOE_CHECK(aligned16(x) && ((uintptr_t)codes & 7u) == 0, "moe_quantize_nvfp4: misaligned buffers");
+  return launch_quant(x, rows, k, input_scale, codes, scales, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,171 @@
+// Shared device helpers for the gfx950 MoE-FP4 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_fp4.h"
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- host side
+void set_error(const char* fmt, ...);
+moe_status launch_status(const char* what);
+
+// ------------------------------------------------------------- bf16 helpers
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// float -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+}
+
+// --------------------------------------------------------- scale decoders
+// E8M0 byte -> float 2^(b-127); 0xFF -> NaN; 0x00 -> 2^-127 (a float subnormal).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
+  if (b == 0xFFu) return __uint_as_float(0x7FC00000u);
+  if (b == 0u) return __uint_as_float(0x00400000u);
+  return __uint_as_float(b << 23);
+}
+
+// E4M3 (FN) byte -> float (exact).  0x7F / 0xFF -> NaN.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  uint32_t e = (b >> 3) & 0xFu, m = b & 7u;
+  float mag;
+  if ((b & 0x7Fu) == 0x7Fu) mag = __uint_as_float(0x7FC00000u);
+  else if (e == 0) mag = (float)m * 0.001953125f;                  // m * 2^-9
+  else mag = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (b & 0x80u) ? -mag : mag;
+}
+
+__device__ __forceinline__ bool is_pow2_scale(float s) {
+  uint32_t u = __float_as_uint(s);
+  uint32_t e = (u >> 23) & 0xFFu;
+  return (u & 0x007FFFFFu) == 0 && e != 0 && e != 0xFFu;
+}
+
+// ------------------------------------------------------- FP4 -> bf16 x 8
+// 8 E2M1 codes (one dword, element 0 in the low nibble) times `scale` -> 8 bf16.
+// The gfx950 convert instruction applies only the power-of-two part of its
+// scale operand; the exact general path goes through float.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16_pow2(uint32_t codes, float pow2_scale) {
+  bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, pow2_scale, 0);
+  bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, pow2_scale, 1);
+  bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, pow2_scale, 2);
+  bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, pow2_scale, 3);
+  bf16x8 r = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16_general(uint32_t codes, float scale) {
+  bf16x8 r;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    f32x2 v;
+    switch (b) {   // the selector must be a constant
+      case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0); break;
+      case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1); break;
+      case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2); break;
+      default: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3); break;
+    }
+    // code (2 significant bits) x E4M3 scale (4 bits): exact in float and in bf16
+    uint32_t w = pack_bf16x2(v[0] * scale, v[1] * scale);
+    bf16x2 p = __builtin_bit_cast(bf16x2, w);
+    r[2 * b] = p[0];
+    r[2 * b + 1] = p[1];
+  }
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t codes, float scale) {
+  if (is_pow2_scale(scale)) return fp4x8_to_bf16_pow2(codes, scale);
+  return fp4x8_to_bf16_general(codes, scale);
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// -------------------------------------------------- NVFP4 quantisation
+// Round a non-negative float to E4M3 (nearest even, saturating at 448).  The
+// input is an exactly-known float (the caller guarantees a single rounding).
+__device__ __forceinline__ uint32_t f32_to_e4m3_sat(float v) {
+  if (!(v > 0.0f)) return 0u;
+  if (v >= 448.0f) return 0x7Eu;
+  uint32_t u = __float_as_uint(v);
+  int e = (int)((u >> 23) & 0xFF) - 127;             // v = 1.f * 2^e
+  if (e < -6) {
+    // subnormal range: value = M * 2^-9, M = rne(v * 2^9) in 0..8 (8 -> min normal 0x08)
+    float t = v * 512.0f;                             // exact (power-of-two scaling)
+    float r = __builtin_rintf(t);                     // round half to even
+    return (uint32_t)r;                               // 0..8; 8 == 0x08 == 2^-6
+  }
+  // normal: keep 3 mantissa bits, round to nearest even on the float bits
+  uint32_t mant = u & 0x7FFFFFu;
+  uint32_t keep = mant >> 20, rest = mant & 0xFFFFFu;
+  uint32_t half = 0x80000u;
+  if (rest > half || (rest == half && (keep & 1u))) keep += 1;
+  uint32_t ee = (uint32_t)(e + 7);
+  if (keep == 8) { keep = 0; ee += 1; }
+  uint32_t byte = (ee << 3) | keep;
+  return byte > 0x7Eu ? 0x7Eu : byte;
+}
+
+// E2M1 magnitude code for |x| / s by exact comparison against the midpoints
+// times s (every product has <= 7 significant bits, so it is exact in float).
+// Ties go to the even code.
+__device__ __forceinline__ uint32_t e2m1_code(float ax, float s) {
+  // midpoints between codes k and k+1, and whether the tie rounds up (to k+1 even)
+  const float m0 = 0.25f * s, m1 = 0.75f * s, m2 = 1.25f * s, m3 = 1.75f * s;
+  const float m4 = 2.5f * s, m5 = 3.5f * s, m6 = 5.0f * s;
+  uint32_t c = 0;
+  c += (ax > m0);                  // tie at 0.25 -> 0 (even)
+  c += (ax >= m1);                 // tie at 0.75 -> 2 (even)
+  c += (ax > m2);                  // tie at 1.25 -> 2
+  c += (ax >= m3);                 // tie at 1.75 -> 4
+  c += (ax > m4);                  // tie at 2.5  -> 4
+  c += (ax >= m5);                 // tie at 3.5  -> 6
+  c += (ax > m6);                  // tie at 5    -> 6
+  return c;
+}
+
+// Quantise 16 floats (exact bf16 values) with global scale g (power of two).
+// Writes 8 code bytes (as two dwords) and returns the E4M3 scale byte.
+__device__ __forceinline__ uint32_t quant16(const float* x, float inv_g, uint32_t& lo, uint32_t& hi) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  // s = E4M3(amax / (6 g)): amax * inv_g is exact, the division is correctly rounded
+  float target = (amax * inv_g) / 6.0f;
+  uint32_t sb = f32_to_e4m3_sat(target);
+  float s = e4m3_to_f32(sb);
+  uint32_t w[2] = {0u, 0u};
+  if (s > 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float xs = x[i] * inv_g;                        // exact
+      uint32_t c = e2m1_code(fabsf(xs), s);
+      uint32_t nib = c | ((__float_as_uint(xs) >> 28) & 8u);   // sign of x
+      w[i >> 3] |= nib << (4 * (i & 7));
+    }
+  }
+  lo = w[0];
+  hi = w[1];
+  return sb;
+}
+
+}  // namespace moe

@@ -1,0 +1,66 @@
+// Arguments and shared pieces of the grouped FP4 expert GEMM kernels.
+#pragma once
+#include "common.h"
+
+namespace moe {
+
+struct GemmArgs {
+  // activations A [rows_src, K]: bf16, or NVFP4 codes [rows_src, K/2] + E4M3 scales [rows_src, K/16]
+  const uint8_t* a_data;
+  const uint8_t* a_scales;
+  float a_gscale;                 // NVFP4 global scale (power of two)
+  const int32_t* gather;          // permuted row r reads source row gather[r] / gather_div
+  int gather_div;
+  // weights [E, N, K]: codes [E, N, K/2]; MX E8M0 [E, N, K/32] | NV E4M3 [E, N, K/16] + float [E]
+  const uint8_t* w_packed[2];
+  const uint8_t* w_scale[2];
+  const float* w_global[2];
+  int E, N, K;
+  int64_t rows;                   // rows of the output (bound for every row index)
+  const int32_t* offsets;         // [E+1]
+  // outputs
+  uint16_t* out_bf16;             // [rows, N] or null
+  uint8_t* out_codes;             // [rows, N/2] or null
+  uint8_t* out_scales;            // [rows, N/16]
+  float out_inv_g;                // 1 / output global scale
+};
+
+// Locate the j-th expert with at least one row (experts in index order).
+// Returns false when fewer than j+1 experts are active.  All threads of the
+// block must call it.
+__device__ __forceinline__ bool find_active_expert(const int32_t* __restrict__ offsets, int E, int64_t rows, int j,
+                                                   int& e_out, int& r0, int& r1) {
+  __shared__ int s_e;
+  __shared__ int s_wc[16];
+  const int nthr = blockDim.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = nthr >> 6;
+  if (threadIdx.x == 0) s_e = -1;
+  int running = 0;
+  for (int e0 = 0; e0 < E; e0 += nthr) {
+    int e = e0 + threadIdx.x;
+    bool act = e < E && offsets[e + 1] > offsets[e];
+    uint64_t b = __ballot(act);
+    if (lane == 0) s_wc[w] = __popcll(b);
+    __syncthreads();
+    int before = running;
+    for (int i = 0; i < w; ++i) before += s_wc[i];
+    int rank = before + __popcll(b & ((1ull << lane) - 1ull));
+    if (act && rank == j) s_e = e;
+    int tot = 0;
+    for (int i = 0; i < nw; ++i) tot += s_wc[i];
+    running += tot;
+    __syncthreads();
+    if (running > j) break;
+  }
+  __syncthreads();
+  int e = s_e;
+  if (e < 0) return false;
+  e_out = e;
+  // rows outside [0, rows) are never touched, whatever the offsets hold
+  r0 = (int)max((int64_t)0, min((int64_t)offsets[e], rows));
+  r1 = (int)max((int64_t)r0, min((int64_t)offsets[e + 1], rows));
+  return r1 > r0;
+}
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+
+}  // namespace moe

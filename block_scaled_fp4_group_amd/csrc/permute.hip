@@ -1,0 +1,247 @@
+// Deterministic token permutation: a stable counting sort of the (token, k)
+// slots by expert over LDS-staged chunks of 2048 slots.
+//
+//   count:   each block histograms its chunk in LDS and writes one row of a
+//            [blocks, E] count table (integer LDS atomics: exact, order-free);
+//   scan:    one block turns the table into per-(block, expert) base rows and
+//            the expert_offsets exclusive prefix sum;
+//   scatter: each block ranks its slots stably inside the chunk -- wave-level
+//            multisplit (the lanes holding the same expert are found with one
+//            ballot per expert-id bit), then a prefix over the chunk's 64-slot
+//            sub-chunks in LDS -- and writes sorted_slots and slot_rows.
+// A single chunk (R <= 2048, every decode batch) runs all three steps in one
+// block and one launch.  Nothing depends on the order in which atomics or
+// blocks execute, so every run gives identical bytes.  The pages only imply
+// this step: one grouped kernel runs over the routed experts ("MiMo-V2.6-Flash-
+// MOPD on one RTX PRO 6000", "What makes it fast", speed v4).
+#include "common.h"
+
+namespace moe {
+
+constexpr int kPermThreads = 256;
+constexpr int kPermChunk = 2048;                                  // slots per block
+constexpr int kPermSub = kPermChunk / kWave;                      // 32 sub-chunks of 64 slots
+constexpr int kSubPerWave = kPermSub / (kPermThreads / kWave);    // 8 per wave
+constexpr int kPermMaxE = 1024;
+constexpr int kERange = 256;                                      // experts per LDS pass
+
+size_t permute_ws_bytes(int64_t R, int E) {
+  int64_t blocks = (R + kPermChunk - 1) / kPermChunk;
+  if (blocks < 1) blocks = 1;
+  return (size_t)blocks * (size_t)E * sizeof(int32_t);
+}
+
+// Ranks of this wave's 8 sub-chunks: expert id (-1 when absent/invalid), rank
+// among equal ids inside the 64-slot sub-chunk, and the group size.
+struct SubRanks {
+  int e[kSubPerWave];
+  int rank[kSubPerWave];
+  int size[kSubPerWave];
+};
+
+__device__ __forceinline__ void rank_subchunks(const int32_t* __restrict__ ids, int64_t R, int E, int nbits,
+                                               int64_t base, SubRanks& r) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int q = 0; q < kSubPerWave; ++q) {
+    int sub = w * kSubPerWave + q;
+    int64_t s = base + (int64_t)sub * kWave + lane;
+    int e = -1;
+    if (s < R) {
+      int v = ids[s];
+      if (v >= 0 && v < E) e = v;
+    }
+    uint64_t peers = __ballot(e >= 0);
+    for (int b = 0; b < nbits; ++b) {
+      uint64_t m = __ballot(e >= 0 && ((e >> b) & 1));
+      peers &= ((e >> b) & 1) ? m : ~m;
+    }
+    r.e[q] = e;
+    r.rank[q] = __popcll(peers & ((1ull << lane) - 1ull));
+    r.size[q] = __popcll(peers);
+  }
+}
+
+// cnt[sub][e - e0] <- group sizes of the sub-chunks, then exclusive prefix over
+// the sub-chunks.  Returns (in tot, for threads e-e0 < 256) the chunk total.
+__device__ __forceinline__ void subchunk_prefix(const SubRanks& r, int e0, uint16_t (*cnt)[kERange],
+                                                int32_t* tot) {
+  const int w = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < kPermSub * kERange; i += kPermThreads) (&cnt[0][0])[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kSubPerWave; ++q) {
+    int e = r.e[q];
+    if (e >= e0 && e < e0 + kERange && r.rank[q] == 0) cnt[w * kSubPerWave + q][e - e0] = (uint16_t)r.size[q];
+  }
+  __syncthreads();
+  {
+    int j = threadIdx.x;    // one expert of the range per thread
+    int32_t run = 0;
+    for (int sub = 0; sub < kPermSub; ++sub) {
+      int32_t c = cnt[sub][j];
+      cnt[sub][j] = (uint16_t)run;
+      run += c;
+    }
+    tot[j] = run;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void write_rows(const SubRanks& r, int e0, const uint16_t (*cnt)[kERange],
+                                           const int32_t* ebase /* LDS or global, indexed e - e0 */,
+                                           int64_t R, int64_t base, int32_t* __restrict__ sorted_slots,
+                                           int32_t* __restrict__ slot_rows) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int q = 0; q < kSubPerWave; ++q) {
+    int sub = w * kSubPerWave + q;
+    int64_t s = base + (int64_t)sub * kWave + lane;
+    int e = r.e[q];
+    if (e >= e0 && e < e0 + kERange) {
+      int32_t pos = ebase[e - e0] + (int32_t)cnt[sub][e - e0] + r.rank[q];
+      sorted_slots[pos] = (int32_t)s;
+      slot_rows[s] = pos;
+    } else if (e < 0 && e0 == 0 && s < R) {
+      slot_rows[s] = -1;
+    }
+  }
+}
+
+// Exclusive scan of v over threads (block of 256); returns the exclusive value,
+// total in *total (LDS).
+__device__ __forceinline__ int32_t block_excl_scan(int32_t v, int32_t* wsum, int32_t* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int32_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int32_t y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  int32_t before = 0;
+  for (int i = 0; i < w; ++i) before += wsum[i];
+  if (threadIdx.x == kPermThreads - 1) *total = before + x;
+  __syncthreads();
+  return before + x - v;
+}
+
+// ---------------------------------------------------------- one chunk
+__global__ __launch_bounds__(kPermThreads) void permute_single(const int32_t* __restrict__ ids, int64_t R, int E,
+                                                               int nbits, int32_t* __restrict__ offsets,
+                                                               int32_t* __restrict__ sorted_slots,
+                                                               int32_t* __restrict__ slot_rows) {
+  __shared__ uint16_t cnt[kPermSub][kERange];
+  __shared__ int32_t tot[kERange];
+  __shared__ int32_t wsum[kPermThreads / kWave];
+  __shared__ int32_t range_total;
+  SubRanks r;
+  rank_subchunks(ids, R, E, nbits, 0, r);
+  int32_t carry = 0;
+  for (int e0 = 0; e0 < E; e0 += kERange) {
+    subchunk_prefix(r, e0, cnt, tot);
+    int j = threadIdx.x;
+    int32_t v = (e0 + j < E) ? tot[j] : 0;
+    int32_t ex = block_excl_scan(v, wsum, &range_total);
+    __syncthreads();
+    tot[j] = carry + ex;
+    if (e0 + j < E) offsets[e0 + j] = carry + ex;
+    carry += range_total;
+    __syncthreads();
+    write_rows(r, e0, cnt, tot, R, 0, sorted_slots, slot_rows);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) offsets[E] = carry;
+}
+
+// ------------------------------------------------------ multi-chunk path
+__global__ __launch_bounds__(kPermThreads) void permute_count(const int32_t* __restrict__ ids, int64_t R, int E,
+                                                              int32_t* __restrict__ table) {
+  __shared__ int32_t hist[kPermMaxE];
+  for (int e = threadIdx.x; e < E; e += kPermThreads) hist[e] = 0;
+  __syncthreads();
+  int64_t base = (int64_t)blockIdx.x * kPermChunk;
+  for (int i = threadIdx.x; i < kPermChunk; i += kPermThreads) {
+    int64_t s = base + i;
+    if (s < R) {
+      int e = ids[s];
+      if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kPermThreads) table[(int64_t)blockIdx.x * E + e] = hist[e];
+}
+
+__global__ __launch_bounds__(kPermThreads) void permute_scan(int32_t* __restrict__ table, int nblk, int E,
+                                                             int32_t* __restrict__ offsets) {
+  __shared__ int32_t tot[kPermMaxE];
+  __shared__ int32_t wsum[kPermThreads / kWave];
+  __shared__ int32_t range_total;
+  for (int e = threadIdx.x; e < E; e += kPermThreads) {
+    int32_t run = 0;
+    for (int b = 0; b < nblk; ++b) {
+      int32_t c = table[(int64_t)b * E + e];
+      table[(int64_t)b * E + e] = run;
+      run += c;
+    }
+    tot[e] = run;
+  }
+  __syncthreads();
+  int32_t carry = 0;
+  for (int e0 = 0; e0 < E; e0 += kPermThreads) {
+    int e = e0 + threadIdx.x;
+    int32_t v = e < E ? tot[e] : 0;
+    int32_t ex = block_excl_scan(v, wsum, &range_total);
+    if (e < E) {
+      offsets[e] = carry + ex;
+      tot[e] = carry + ex;
+    }
+    carry += range_total;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) offsets[E] = carry;
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kPermThreads) {
+    int32_t b0 = tot[e];
+    for (int b = 0; b < nblk; ++b) table[(int64_t)b * E + e] += b0;
+  }
+}
+
+__global__ __launch_bounds__(kPermThreads) void permute_scatter(const int32_t* __restrict__ ids, int64_t R, int E,
+                                                                int nbits, const int32_t* __restrict__ table,
+                                                                int32_t* __restrict__ sorted_slots,
+                                                                int32_t* __restrict__ slot_rows) {
+  __shared__ uint16_t cnt[kPermSub][kERange];
+  __shared__ int32_t tot[kERange];
+  const int64_t base = (int64_t)blockIdx.x * kPermChunk;
+  SubRanks r;
+  rank_subchunks(ids, R, E, nbits, base, r);
+  const int32_t* brow = table + (int64_t)blockIdx.x * E;
+  for (int e0 = 0; e0 < E; e0 += kERange) {
+    subchunk_prefix(r, e0, cnt, tot);
+    write_rows(r, e0, cnt, brow + e0, R, base, sorted_slots, slot_rows);
+    __syncthreads();
+  }
+}
+
+moe_status launch_permute(const int32_t* ids, int64_t T, int top_k, int E, int32_t* offsets,
+                          int32_t* sorted_slots, int32_t* slot_rows, void* ws, hipStream_t stream) {
+  int64_t R = T * top_k;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  int64_t nblk = (R + kPermChunk - 1) / kPermChunk;
+  if (nblk <= 1) {
+    hipLaunchKernelGGL(permute_single, dim3(1), dim3(kPermThreads), 0, stream, ids, R, E, nbits, offsets,
+                       sorted_slots, slot_rows);
+    return launch_status("moe_permute");
+  }
+  int32_t* table = (int32_t*)ws;
+  hipLaunchKernelGGL(permute_count, dim3((uint32_t)nblk), dim3(kPermThreads), 0, stream, ids, R, E, table);
+  hipLaunchKernelGGL(permute_scan, dim3(1), dim3(kPermThreads), 0, stream, table, (int)nblk, E, offsets);
+  hipLaunchKernelGGL(permute_scatter, dim3((uint32_t)nblk), dim3(kPermThreads), 0, stream, ids, R, E, nbits,
+                     table, sorted_slots, slot_rows);
+  return launch_status("moe_permute");
+}
+
+}  // namespace moe

@@ -1,0 +1,80 @@
+"""One routed-expert MoE layer composed from the five C-ABI calls.
+
+route -> permute -> [W4A4: quantise x] -> gate/up grouped GEMM with SwiGLU
+(writes z, bf16 or NVFP4) -> down grouped GEMM -> weighted combine.  Buffers
+are allocated once for a maximum token count, so a forward pass allocates
+nothing and can be captured in a HIP graph.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import torch
+
+from . import (MOE_ALGO_AUTO, Weights, combine, grouped_gemm, permute, permute_workspace_bytes, quantize_nvfp4,
+               route)
+
+
+@dataclasses.dataclass
+class LayerWeights:
+    gate: Weights     # [E, I, H]
+    up: Weights       # [E, I, H]
+    down: Weights     # [E, H, I]
+
+
+class MoELayer:
+    def __init__(self, weights: LayerWeights, num_experts: int, n_group: int, topk_group: int, top_k: int,
+                 routed_scaling_factor: float, max_tokens: int, act_mode: str = "bf16", input_scale: float = 1.0,
+                 keep_z_bf16: bool = False, device="cuda"):
+        self.w = weights
+        self.E, self.n_group, self.topk_group, self.top_k = num_experts, n_group, topk_group, top_k
+        self.scale = routed_scaling_factor
+        self.act_mode = act_mode
+        self.input_scale = input_scale
+        E, I, H2 = weights.gate.packed.shape
+        H = 2 * H2
+        self.H, self.I = H, I
+        T, R = max_tokens, max_tokens * top_k
+        dev = torch.device(device)
+        i32 = torch.int32
+        self.ids = torch.empty((T, top_k), dtype=i32, device=dev)
+        self.topw = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+        self.offsets = torch.empty(E + 1, dtype=i32, device=dev)
+        self.sorted_slots = torch.empty(R, dtype=i32, device=dev)
+        self.slot_rows = torch.empty(R, dtype=i32, device=dev)
+        self.ws = torch.empty(max(permute_workspace_bytes(T, top_k, E), 16), dtype=torch.uint8, device=dev)
+        self.o = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+        self.y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        w4a4 = act_mode == "nvfp4"
+        self.z = torch.empty((R, I), dtype=torch.bfloat16, device=dev) if (not w4a4 or keep_z_bf16) else None
+        if w4a4:
+            self.x_codes = torch.empty((T, H // 2), dtype=torch.uint8, device=dev)
+            self.x_scales = torch.empty((T, H // 16), dtype=torch.uint8, device=dev)
+            self.z_codes = torch.empty((R, I // 2), dtype=torch.uint8, device=dev)
+            self.z_scales = torch.empty((R, I // 16), dtype=torch.uint8, device=dev)
+
+    def forward(self, x: torch.Tensor, logits: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                residual: Optional[torch.Tensor] = None, algo: int = MOE_ALGO_AUTO, y: Optional[torch.Tensor] = None):
+        T = x.shape[0]
+        R = T * self.top_k
+        ids, topw = self.ids[:T], self.topw[:T]
+        route(logits, bias, self.E, self.n_group, self.topk_group, self.top_k, self.scale, True, ids=ids, weights=topw)
+        permute(ids, self.E, self.ws, self.offsets, self.sorted_slots[:R], self.slot_rows[:R])
+        z = None if self.z is None else self.z[:R]
+        o = self.o[:R]
+        if self.act_mode == "nvfp4":
+            xc, xs = quantize_nvfp4(x, self.input_scale, self.x_codes[:T], self.x_scales[:T])
+            grouped_gemm(xc, self.w.gate, self.w.up, self.offsets, R, gather=self.sorted_slots[:R],
+                         gather_div=self.top_k, a_scales=xs, input_scale=self.input_scale, out=z,
+                         out_codes=self.z_codes[:R], out_scales=self.z_scales[:R], output_scale=self.input_scale,
+                         want_bf16=z is not None, algo=algo)
+            grouped_gemm(self.z_codes[:R], self.w.down, None, self.offsets, R, a_scales=self.z_scales[:R],
+                         input_scale=self.input_scale, out=o, algo=algo)
+        else:
+            grouped_gemm(x, self.w.gate, self.w.up, self.offsets, R, gather=self.sorted_slots[:R],
+                         gather_div=self.top_k, out=z, algo=algo)
+            grouped_gemm(z, self.w.down, None, self.offsets, R, out=o, algo=algo)
+        y = self.y[:T] if y is None else y
+        combine(o, self.slot_rows[:R], topw, residual, y=y)
+        return y

@@ -106,18 +106,27 @@ def unpack_codes(packed: np.ndarray) -> np.ndarray:
     return out
 
 
+# value pair of every packed byte: (element 2i = low nibble, element 2i+1 = high nibble)
+_PAIR = np.stack([e2m1_value(np.arange(256) & 0xF), e2m1_value(np.arange(256) >> 4)], axis=-1)
+
+
+def _codes_value(packed: np.ndarray) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    return _PAIR[p].reshape(p.shape[:-1] + (p.shape[-1] * 2,))
+
+
 def dequant_mx(packed: np.ndarray, scale: np.ndarray) -> np.ndarray:
     """MXFP4 [.., n, k/2] codes + [.., n, k/32] E8M0 -> float64 [.., n, k]."""
-    v = e2m1_value(unpack_codes(packed))
-    s = np.repeat(e8m0_value(scale), 32, axis=-1)
-    return v * s
+    v = _codes_value(packed)
+    s = e8m0_value(scale)
+    return (v.reshape(s.shape + (32,)) * s[..., None]).reshape(v.shape)
 
 
 def dequant_nv(packed: np.ndarray, scale: np.ndarray, global_scale) -> np.ndarray:
     """NVFP4 [.., n, k/2] codes + [.., n, k/16] E4M3 + global -> float64 [.., n, k]."""
-    v = e2m1_value(unpack_codes(packed))
-    s = np.repeat(e4m3_value(scale), 16, axis=-1)
+    v = _codes_value(packed)
+    s = e4m3_value(scale)
     g = np.asarray(global_scale, dtype=np.float64)
     if g.ndim:
-        g = g.reshape(g.shape + (1,) * (v.ndim - g.ndim))
-    return v * s * g
+        g = g.reshape(g.shape + (1,) * (s.ndim - g.ndim))
+    return (v.reshape(s.shape + (16,)) * (s * g)[..., None]).reshape(v.shape)

@@ -1,0 +1,102 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every
+function the header declares, and rejects bad arguments before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_fp4.h")
+
+moe = pytest.importorskip("block_scaled_fp4_group_amd")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "extern")))
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for n in ("moe_route", "moe_permute", "moe_fp4_grouped_gemm", "moe_combine", "fp4_transcode_mx_to_nv"):
+        assert n in names
+
+
+def test_every_declared_function_is_exported():
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in the header but not exported"
+    assert set(moe.EXPORTS) == set(names)
+
+
+def _err(status, expect):
+    assert status == expect, (status, moe.lib.moe_last_error())
+    assert moe.lib.moe_last_error()
+
+
+FAKE = ctypes.c_void_p(0x10000)     # an aligned non-null address; never dereferenced on error paths
+
+
+def test_route_rejects_bad_params():
+    for p in [moe.RouteParams(257, 8, 4, 8, 2.827, 1), moe.RouteParams(256, 7, 4, 8, 2.827, 1),
+              moe.RouteParams(256, 8, 9, 8, 2.827, 1), moe.RouteParams(256, 8, 4, 17, 2.827, 1),
+              moe.RouteParams(32, 8, 1, 5, 2.827, 1), moe.RouteParams(8, 8, 4, 2, 1.0, 1)]:
+        _err(moe.lib.moe_route(FAKE, None, 4, ctypes.byref(p), FAKE, FAKE, None), moe.MOE_ERR_INVALID)
+    p = moe.RouteParams(256, 8, 4, 8, 2.827, 1)
+    _err(moe.lib.moe_route(None, None, 4, ctypes.byref(p), FAKE, FAKE, None), moe.MOE_ERR_INVALID)
+    assert moe.lib.moe_route(None, None, 0, ctypes.byref(p), None, None, None) == moe.MOE_OK   # T == 0 no-op
+    _err(moe.lib.moe_route(FAKE, None, 4, None, FAKE, FAKE, None), moe.MOE_ERR_INVALID)
+
+
+def test_permute_workspace_and_limits():
+    assert moe.lib.moe_permute_workspace_bytes(16384, 8, 128) >= 64 * 128 * 4
+    _err(moe.lib.moe_permute(FAKE, 4096, 8, 256, FAKE, FAKE, FAKE, FAKE, 16, None), moe.MOE_ERR_WORKSPACE)
+    _err(moe.lib.moe_permute(FAKE, 4, 8, 2000, FAKE, FAKE, FAKE, None, 0, None), moe.MOE_ERR_INVALID)
+    _err(moe.lib.moe_permute(FAKE, 4, 8, 256, None, FAKE, FAKE, None, 0, None), moe.MOE_ERR_INVALID)
+
+
+def _w(fmt=moe.MOE_FP4_MX, E=4, n=256, k=512, glob=None):
+    return moe.Fp4Weights(fmt, E, n, k, 0x10000, 0x20000, glob)
+
+
+def _gemm(act, w0, w1, epi=moe.MOE_EPI_SWIGLU, rows=8, out=None, algo=0):
+    out = out or moe.Out(0x30000, None, None, 1.0)
+    return moe.lib.moe_fp4_grouped_gemm(ctypes.byref(act), ctypes.byref(w0), None if w1 is None else ctypes.byref(w1),
+                                        epi, FAKE, rows, ctypes.byref(out), algo, None)
+
+
+def test_gemm_rejects_bad_arguments():
+    act = moe.Act(moe.MOE_ACT_BF16, 0x40000, None, 1.0, None, 1, 8)
+    _err(_gemm(act, _w(k=160), _w(k=160)), moe.MOE_ERR_UNSUPPORTED)          # k % 128
+    _err(_gemm(act, _w(), _w(n=128)), moe.MOE_ERR_INVALID)                     # w0 / w1 differ
+    _err(_gemm(act, _w(), None), moe.MOE_ERR_INVALID)                          # SwiGLU needs w1
+    _err(_gemm(act, _w(fmt=moe.MOE_FP4_NV), _w(fmt=moe.MOE_FP4_NV)), moe.MOE_ERR_INVALID)   # NV without global
+    bad = moe.Act(moe.MOE_ACT_NVFP4, 0x40000, 0x50000, 3.0, None, 1, 8)
+    _err(_gemm(bad, _w(), _w()), moe.MOE_ERR_INVALID)                          # non power-of-two input scale
+    unal = moe.Act(moe.MOE_ACT_BF16, 0x40008, None, 1.0, None, 1, 8)
+    _err(_gemm(unal, _w(), _w()), moe.MOE_ERR_INVALID)                         # misaligned activations
+    _err(_gemm(act, _w(), _w(), out=moe.Out(None, None, None, 1.0)), moe.MOE_ERR_INVALID)   # no output
+    _err(_gemm(act, _w(), _w(), algo=7), moe.MOE_ERR_INVALID)
+    assert _gemm(act, _w(), _w(), rows=0) == moe.MOE_OK                        # zero rows: no-op
+
+
+def test_combine_transcode_quant_reject():
+    _err(moe.lib.moe_combine(FAKE, FAKE, FAKE, None, 4, 8, 12, FAKE, None), moe.MOE_ERR_INVALID)   # h % 8
+    _err(moe.lib.moe_combine(None, FAKE, FAKE, None, 4, 8, 16, FAKE, None), moe.MOE_ERR_INVALID)
+    cnt = ctypes.c_void_p(0x60000)
+    _err(moe.lib.fp4_transcode_mx_to_nv(FAKE, FAKE, 2, 16, 48, FAKE, FAKE, cnt, None), moe.MOE_ERR_INVALID)
+    _err(moe.lib.fp4_transcode_mx_to_nv(FAKE, FAKE, 2, 8, 64, FAKE, FAKE, cnt, None), moe.MOE_ERR_INVALID)
+    _err(moe.lib.fp4_transcode_mx_to_nv(FAKE, FAKE, 2, 16, 64, FAKE, FAKE, None, None), moe.MOE_ERR_INVALID)
+    _err(moe.lib.moe_quantize_nvfp4(FAKE, 4, 48, 1.0, FAKE, FAKE, None), moe.MOE_ERR_INVALID)
+    _err(moe.lib.moe_quantize_nvfp4(FAKE, 4, 64, 0.3, FAKE, FAKE, None), moe.MOE_ERR_INVALID)
+    assert moe.lib.moe_quantize_nvfp4(None, 0, 64, 1.0, None, None, None) == moe.MOE_OK
+
+
+def test_status_strings():
+    for s in range(5):
+        assert moe.lib.moe_status_string(s)

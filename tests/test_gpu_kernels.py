@@ -1,0 +1,336 @@
+"""GPU parity of each kernel against the CPU oracle, through the C ABI.
+
+Exact comparisons for integer / byte results (routing ids, permutation,
+transcoded scales and counters, NVFP4 codes); max|err| <= 2e-2 * rms for
+floating-point outputs; router weights to rtol 1e-6.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import (BF16_ULP, assert_close_rms, bf16_to_f64, dev_bf16, dev_f32, dev_i32, dev_u8, host, host_bf16_bits,
+                      say)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import block_scaled_fp4_group_amd as moe  # noqa: E402
+
+
+def test_native_library_is_loaded():
+    maps = open("/proc/self/maps").read()
+    assert "libmoefp4.so" in maps
+    hip = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    say("  HIP runtime(s):", hip)
+    assert len(hip) == 1, f"more than one HIP runtime mapped: {hip}"
+    assert moe.lib.moe_version().decode().startswith("moe_fp4")
+
+
+# ------------------------------------------------------------------ route
+ROUTE_CASES = [
+    ("tiny", 32, False), ("decode", 1, False), ("decode", 64, False), ("prefill", 8192, True),
+    ("reap50", 16384, False),
+]
+
+
+@pytest.mark.parametrize("name,T,with_bias", ROUTE_CASES)
+def test_route_parity(name, T, with_bias):
+    w = synth.WORKLOADS[name]
+    s = w.shape
+    say(f"route {name} T={T}")
+    l = synth.logits(w, T)
+    bias = synth.correction_bias(w) if with_bias else None
+    r = oracle.route(l, bias, s.n_group, s.topk_group, s.top_k, s.routed_scaling_factor)
+    ids, wts = moe.route(dev_f32(l), None if bias is None else dev_f32(bias), s.num_experts, s.n_group,
+                         s.topk_group, s.top_k, s.routed_scaling_factor)
+    torch.cuda.synchronize()
+    gi, gw = host(ids), host(wts)
+    ok = ~r.near_tie
+    say(f"  near-ties flagged: {int((~ok).sum())}")
+    assert np.array_equal(gi[ok], r.ids[ok])
+    np.testing.assert_allclose(gw[ok], r.weights[ok], rtol=1e-6)
+
+
+def test_route_ties_and_edge_cases():
+    # all-equal scores, duplicated logits across groups, a strong bias, tiny T
+    E = 256
+    l = np.zeros((6, E), np.float32)
+    l[1] = synth.random_logits(1, 1, E)[0]
+    l[1, 100] = l[1, 7]                      # exact duplicate in another group
+    l[2, :] = 3.0
+    l[2, ::17] = 5.0
+    l[3] = synth.random_logits(2, 1, E)[0] * 8          # saturating sigmoids
+    l[4] = -l[3]
+    l[5] = synth.random_logits(3, 1, E)[0]
+    bias = np.zeros(E, np.float32)
+    bias[[5, 99, 200]] = [0.3, -0.2, 0.7]
+    for b in (None, bias):
+        r = oracle.route(l, b, 8, 4, 8, 2.827)
+        ids, wts = moe.route(dev_f32(l), None if b is None else dev_f32(b), E, 8, 4, 8, 2.827)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(ids), r.ids)
+        np.testing.assert_allclose(host(wts), r.weights, rtol=1e-6)
+
+
+@pytest.mark.parametrize("E,n_group,topk_group,top_k", [(64, 4, 2, 6), (128, 8, 4, 8), (16, 2, 1, 3)])
+def test_route_other_shapes(E, n_group, topk_group, top_k):
+    l = synth.random_logits(E, 257, E)
+    r = oracle.route(l, None, n_group, topk_group, top_k, 1.5)
+    ids, wts = moe.route(dev_f32(l), None, E, n_group, topk_group, top_k, 1.5)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(ids), r.ids)
+    np.testing.assert_allclose(host(wts), r.weights, rtol=1e-6)
+
+
+# ---------------------------------------------------------------- permute
+@pytest.mark.parametrize("T,E,invalid", [(0, 32, False), (1, 256, False), (7, 32, False), (64, 256, False),
+                                          (255, 256, False), (300, 128, True), (4096, 256, False),
+                                          (16384, 128, False), (2000, 1024, True)])
+def test_permute_parity(T, E, invalid):
+    rng = np.random.default_rng(T * 7 + E)
+    ids = rng.integers(0, E, size=(T, 8)).astype(np.int32)
+    if T > 100:     # skew: a few experts take many slots
+        hot = rng.random((T, 8)) < 0.3
+        ids[hot] = rng.integers(0, 3, size=int(hot.sum()))
+    if invalid and T:
+        ids[0, 0] = -1
+        ids[T // 2, 3] = E
+    say(f"permute T={T} E={E}")
+    valid = (ids >= 0) & (ids < E)
+    off_ref, ss_ref, sr_ref = oracle.permute(np.where(valid, ids, 0), E)
+    off, ss, sr = moe.permute(dev_i32(ids), E)
+    torch.cuda.synchronize()
+    if invalid and T:
+        # reference with the invalid slots removed
+        flat = ids.ravel()
+        keep = np.flatnonzero(valid.ravel())
+        order = keep[np.argsort(flat[keep], kind="stable")]
+        counts = np.bincount(flat[keep], minlength=E)
+        off_ref = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        ss_ref = order.astype(np.int32)
+        sr_ref = np.full(flat.size, -1, np.int32)
+        sr_ref[order] = np.arange(order.size)
+        n = order.size
+        assert np.array_equal(host(off), off_ref)
+        assert np.array_equal(host(ss)[:n], ss_ref)
+        assert np.array_equal(host(sr), sr_ref)
+        return
+    assert np.array_equal(host(off), off_ref)
+    assert np.array_equal(host(ss), ss_ref)
+    assert np.array_equal(host(sr), sr_ref)
+
+
+# --------------------------------------------------------------- quantise
+@pytest.mark.parametrize("g", [1.0, 0.5, 4.0])
+def test_quantize_nvfp4_parity(g):
+    rng = np.random.default_rng(11)
+    rows, k = 203, 512
+    x = (rng.standard_normal((rows, k)) * 10.0 ** rng.integers(-4, 4, (rows, 1))).astype(np.float32)
+    x[0, :16] = np.array([6, 5, 4, 3.5, 3, 2.5, 2, 1.75, 1.5, 1.25, 1, .75, .5, .25, 0, -0.0]) * 3.0
+    x[1, :32] = 0.0
+    x[1, 32:48] = 1e-5
+    x[2, 16:32] = -0.0
+    for j, amax in enumerate(synth.OUTLIER_AMAX + (2688.0,)):
+        x[3 + j, 5] = amax
+        x[3 + j, 40] = -amax
+    xb = synth.bf16_bits_from_f32(x)
+    c_ref, s_ref = oracle.quantize_nvfp4(xb, g)
+    c, s = moe.quantize_nvfp4(dev_bf16(xb), g)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(s), s_ref)
+    assert np.array_equal(host(c), c_ref)
+
+
+def test_quantize_nvfp4_outlier_rows():
+    z = synth.down_inputs_with_outliers(256, 2048, 311296.0)
+    c_ref, s_ref = oracle.quantize_nvfp4(z, 1.0)
+    c, s = moe.quantize_nvfp4(dev_bf16(z), 1.0)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(s), s_ref)
+    assert np.array_equal(host(c), c_ref)
+    v = oracle.dequant_nvfp4_act(host(c), host(s))
+    assert np.max(np.abs(v)) == 2688.0
+
+
+# -------------------------------------------------------------- transcode
+def _transcode_case(mx, packed):
+    nv_ref, g_ref, cnt_ref = oracle.transcode_mx_to_nv(mx, packed)
+    nv, g, cnt = moe.transcode_mx_to_nv(dev_u8(mx), dev_u8(packed))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(nv), nv_ref)
+    assert np.array_equal(host(g).view(np.uint32), g_ref.view(np.uint32))
+    c = host(cnt)
+    assert list(c) == [cnt_ref["blocks"], cnt_ref["zero_oor"], cnt_ref["rerounded"], cnt_ref["nan"]]
+    return c
+
+
+def test_transcode_parity_random():
+    packed, mx = synth.random_mx_small(21, 12, 64, 512)
+    c = _transcode_case(mx, packed)
+    assert c[2] == 0 and c[1] == 0
+
+
+def test_transcode_parity_edge_blocks():
+    packed, mx = synth.random_mx_small(22, 5, 32, 256, lo=90, hi=140)
+    mx = mx.copy()
+    packed = packed.copy()
+    mx[0, 0, 0] = 200                  # large span: many blocks out of range
+    mx[1, 3, 2] = 255                  # NaN
+    mx[2, 5, 1] = 0                    # 2^-127
+    packed[2, 5, 16:32] = 0x80         # all -0 codes -> all-zero block
+    mx[3] = 255                        # a matrix with no finite block
+    mx[4, :, :] = 127
+    mx[4, 0, 0] = 127 + 17             # span 17 exactly
+    mx[4, 1, 0] = 127 - 1              # span 18 -> re-rounded
+    c = _transcode_case(mx, packed)
+    assert c[1] >= 1 and c[2] >= 1 and c[3] >= 32 * 8
+
+
+def test_transcode_parity_full_matrix_shape():
+    # a few matrices at the real [2048, 4096] and [4096, 2048] shapes
+    w = synth.WORKLOADS["decode"]
+    W = synth.expert_weights(w, experts=[0, 1, 2])
+    for name in ("gate", "down"):
+        packed, mx = W[name]
+        c = _transcode_case(mx, packed)
+        assert c[1] == 0 and c[2] == 0
+
+
+# ---------------------------------------------------------------- combine
+@pytest.mark.parametrize("with_resid", [False, True])
+def test_combine_parity(with_resid):
+    rng = np.random.default_rng(5)
+    T, k, h = 37, 8, 512
+    R = T * k
+    o = synth.random_bf16(31, (R, h))
+    perm = rng.permutation(R).astype(np.int32)
+    perm[3] = -1
+    wts = rng.uniform(0.05, 1.0, (T, k)).astype(np.float32)
+    resid = synth.random_bf16(32, (T, h)) if with_resid else None
+    y = moe.combine(dev_bf16(o), dev_i32(perm), dev_f32(wts), None if resid is None else dev_bf16(resid))
+    torch.cuda.synchronize()
+    ov = bf16_to_f64(o)
+    gathered = np.where(perm[:, None] >= 0, ov[np.maximum(perm, 0)], 0.0).reshape(T, k, h)
+    ref = oracle.combine(gathered, wts.astype(np.float64), resid)
+    got = bf16_to_f64(host_bf16_bits(y))
+    assert_close_rms(got, bf16_to_f64(ref), what="combine y", ulp_rel=BF16_ULP)
+    # one bf16 rounding of an FP32 sum: at most one bf16 ulp from the float64 result
+    refv = bf16_to_f64(ref)
+    assert np.all(np.abs(got - refv) <= np.abs(refv) * 2 ** -7 + 1e-30)
+
+
+# ------------------------------------------------------------ grouped GEMM
+def _gemm_problem(seed, E, n, k, counts, nsrc, fmt, general_nv=False):
+    rng = np.random.default_rng(seed)
+    packed, mx = synth.random_mx_small(seed, E, n, k)
+    if fmt == "mx":
+        wt = (packed, mx)
+        dq = [oracle.dequant_mx(packed[e], mx[e]) for e in range(E)]
+        wdev = moe.Weights(dev_u8(packed), dev_u8(mx))
+    else:
+        if general_nv:
+            sc = rng.integers(0x20, 0x60, size=(E, n, k // 16)).astype(np.uint8)   # arbitrary E4M3 scales
+            g = rng.uniform(0.3, 3.0, E).astype(np.float32)
+        else:
+            sc, g, _ = oracle.transcode_mx_to_nv(mx, packed)
+        wt = (packed, sc, g)
+        dq = [oracle.dequant_nv(packed[e], sc[e], g[e]) for e in range(E)]
+        wdev = moe.Weights(dev_u8(packed), dev_u8(sc), dev_f32(g))
+    return wdev, dq
+
+
+GEMM_COUNTS = [0, 1, 17, 300, 1000, 33, 0, 64]
+
+
+@pytest.mark.parametrize("algo", [moe.MOE_ALGO_DECODE, moe.MOE_ALGO_PREFILL])
+@pytest.mark.parametrize("fmt,general", [("mx", False), ("nv", False), ("nv", True)])
+@pytest.mark.parametrize("amode", ["bf16", "nvfp4"])
+def test_grouped_gemm_swiglu_parity(algo, fmt, general, amode):
+    E, H, I = 8, 512, 256
+    counts = np.array(GEMM_COUNTS)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offsets[-1])
+    tsrc = 700
+    say(f"gemm swiglu algo={algo} fmt={fmt} general={general} amode={amode} R={R}")
+    x = synth.random_bf16(41, (tsrc, H))
+    rng = np.random.default_rng(42)
+    gather = rng.integers(0, tsrc * 8, size=R).astype(np.int32)          # slot ids; row = slot // 8
+    wg, dg = _gemm_problem(43, E, I, H, counts, tsrc, fmt, general)
+    wu, du = _gemm_problem(44, E, I, H, counts, tsrc, fmt, general)
+    if amode == "nvfp4":
+        xc, xs = oracle.quantize_nvfp4(x, 1.0)
+        a_val = oracle.dequant_nvfp4_act(xc, xs)
+        a_dev, a_sc = dev_u8(xc), dev_u8(xs)
+    else:
+        a_val = bf16_to_f64(x)
+        a_dev, a_sc = dev_bf16(x), None
+    zc = torch.empty((R, I // 2), dtype=torch.uint8, device="cuda")
+    zs = torch.empty((R, I // 16), dtype=torch.uint8, device="cuda")
+    z = moe.grouped_gemm(a_dev, wg, wu, dev_i32(offsets), R, gather=dev_i32(gather), gather_div=8, a_scales=a_sc,
+                         out_codes=zc, out_scales=zs, algo=algo)
+    z2 = moe.grouped_gemm(a_dev, wg, wu, dev_i32(offsets), R, gather=dev_i32(gather), gather_div=8, a_scales=a_sc,
+                          algo=algo)
+    torch.cuda.synchronize()
+    zb = host_bf16_bits(z)
+    assert np.array_equal(zb, host_bf16_bits(z2)), "not deterministic"
+    ref = np.zeros((R, I))
+    for e in range(E):
+        rows = slice(offsets[e], offsets[e + 1])
+        a = a_val[gather[rows] // 8]
+        gt, up = a @ dg[e].T, a @ du[e].T
+        ref[rows] = oracle.silu(gt) * up
+    ref = bf16_to_f64(oracle.round_to_bf16_bits(ref))          # z is stored as bfloat16
+    assert_close_rms(bf16_to_f64(zb), ref, what="z", ulp_rel=BF16_ULP)
+    # NVFP4 output: exactly the oracle's quantisation of the GPU's own bf16 z
+    c_ref, s_ref = oracle.quantize_nvfp4(zb, 1.0)
+    assert np.array_equal(host(zs), s_ref)
+    assert np.array_equal(host(zc), c_ref)
+
+
+@pytest.mark.parametrize("algo", [moe.MOE_ALGO_DECODE, moe.MOE_ALGO_PREFILL])
+@pytest.mark.parametrize("fmt", ["mx", "nv"])
+@pytest.mark.parametrize("amode", ["bf16", "nvfp4"])
+def test_grouped_gemm_down_parity(algo, fmt, amode):
+    E, H, I = 8, 512, 256
+    counts = np.array(GEMM_COUNTS[::-1])
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offsets[-1])
+    say(f"gemm down algo={algo} fmt={fmt} amode={amode} R={R}")
+    z = synth.random_bf16(51, (R + 5, I))
+    wd, dd = _gemm_problem(52, E, H, I, counts, R, fmt)
+    if amode == "nvfp4":
+        zc, zs = oracle.quantize_nvfp4(z, 1.0)
+        a_val = oracle.dequant_nvfp4_act(zc, zs)
+        a_dev, a_sc = dev_u8(zc), dev_u8(zs)
+    else:
+        a_val = bf16_to_f64(z)
+        a_dev, a_sc = dev_bf16(z), None
+    o = moe.grouped_gemm(a_dev, wd, None, dev_i32(offsets), R + 5, a_scales=a_sc, algo=algo)
+    torch.cuda.synchronize()
+    got = bf16_to_f64(host_bf16_bits(o))[:R]
+    ref = np.zeros((R, H))
+    for e in range(E):
+        rows = slice(offsets[e], offsets[e + 1])
+        ref[rows] = a_val[rows] @ dd[e].T
+    assert_close_rms(got, ref, what="o", ulp_rel=BF16_ULP)
+
+
+def test_grouped_gemm_empty_and_invalid():
+    E, H, I = 4, 256, 128
+    wg, _ = _gemm_problem(61, E, I, H, None, 1, "mx")
+    offsets = dev_i32(np.zeros(E + 1, np.int32))
+    x = dev_bf16(synth.random_bf16(62, (4, H)))
+    out = torch.full((4, I), 7.0, dtype=torch.bfloat16, device="cuda")
+    moe.grouped_gemm(x, wg, wg, offsets, 4, out=out)             # every expert empty: nothing written
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.grouped_gemm(x, wg, wg, offsets, 4, out=out, input_scale=3.0,
+                         a_scales=torch.zeros((4, H // 16), dtype=torch.uint8, device="cuda"))
+    assert ei.value.status == moe.MOE_ERR_INVALID

@@ -1,0 +1,229 @@
+"""End-to-end GPU parity of the MoE layer on the five workloads.
+
+Routing and permutation are compared exactly for every token; the expert
+outputs (z, o) and the layer output y are compared on every token of the small
+shapes and on sampled tokens of the full shapes (the oracle evaluates those one
+by one), step-wise: each stage is recomputed by the oracle from the GPU's own
+input to that stage, and the end-to-end error is reported too.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import BF16_ULP, assert_close_rms, bf16_to_f64, dev_bf16, dev_f32, dev_u8, host, host_bf16_bits, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import block_scaled_fp4_group_amd as moe  # noqa: E402
+
+
+class ExpertCache:
+    """float64 dequantised experts for the oracle, one expert at a time."""
+
+    def __init__(self, W, fmt):
+        self.W, self.fmt, self.cache = W, fmt, {}
+
+    def __call__(self, e):
+        if e not in self.cache:
+            if len(self.cache) > 48:
+                self.cache.clear()
+            self.cache[e] = oracle.layer.dequant_expert(self.W, e, self.fmt)
+        return self.cache[e]
+
+
+def upload_weights(W, fmt):
+    def one(name):
+        t = W[name]
+        if fmt == "mx":
+            return moe.Weights(dev_u8(t[0]), dev_u8(t[1]))
+        return moe.Weights(dev_u8(t[0]), dev_u8(t[1]), dev_f32(t[2]))
+    return moe.LayerWeights(one("gate"), one("up"), one("down"))
+
+
+def check_layer(w, T, W, fmt, act_mode, sample, layer_idx=0, residual=None, x=None, algo=moe.MOE_ALGO_AUTO,
+                dev_weights=None, cache=None):
+    s = w.shape
+    say(f"layer {w.name} T={T} fmt={fmt} act={act_mode} layer={layer_idx} algo={algo}")
+    x = synth.activations(w, T, layer_idx) if x is None else x
+    l = synth.logits(w, T, layer_idx)
+    bias = synth.correction_bias(w, layer_idx)
+    dw = upload_weights(W, fmt) if dev_weights is None else dev_weights
+    layer = moe.MoELayer(dw, s.num_experts, s.n_group, s.topk_group, s.top_k, s.routed_scaling_factor, T,
+                         act_mode=act_mode, keep_z_bf16=True)
+    y = layer.forward(dev_bf16(x), dev_f32(l), None if bias is None else dev_f32(bias),
+                      None if residual is None else dev_bf16(residual), algo=algo)
+    torch.cuda.synchronize()
+    R = T * s.top_k
+    ids, topw = host(layer.ids[:T]), host(layer.topw[:T])
+    off, ss, sr = host(layer.offsets), host(layer.sorted_slots[:R]), host(layer.slot_rows[:R])
+    z = host_bf16_bits(layer.z[:R])
+    o = host_bf16_bits(layer.o[:R])
+    yb = host_bf16_bits(y)
+
+    toks = np.arange(T) if sample is None else np.asarray(sample)
+    cache = ExpertCache(W, fmt) if cache is None else cache
+    ref = oracle.moe_layer(x, l, bias, W, s.n_group, s.topk_group, s.top_k, s.routed_scaling_factor, fmt=fmt,
+                           act_mode=act_mode, residual_bits=residual, tokens=toks, expert_loader=cache)
+    ok = ~ref.near_tie
+    say(f"  near-ties flagged: {int((~ok).sum())}")
+    assert np.array_equal(ids[ok], ref.ids[ok])
+    np.testing.assert_allclose(topw[ok], ref.weights[ok], rtol=1e-6)
+    assert np.array_equal(off, ref.offsets)
+    assert np.array_equal(ss, ref.sorted_slots)
+    assert np.array_equal(sr, ref.slot_rows)
+
+    # step-wise expert outputs of the sampled tokens' slots
+    slots = (toks[:, None] * s.top_k + np.arange(s.top_k)[None, :]).ravel()
+    rows = sr[slots]
+    z_gpu = z[rows].reshape(len(toks), s.top_k, -1)
+    assert_close_rms(bf16_to_f64(z_gpu), bf16_to_f64(ref.z), what="z (SwiGLU out)", ulp_rel=BF16_ULP)
+    o_step = np.zeros((len(toks), s.top_k, s.hidden))
+    for i, t in enumerate(toks):
+        for j in range(s.top_k):
+            e = int(ids[t, j])
+            wd = cache(e)[2]
+            if act_mode == "nvfp4":
+                zc = host(layer.z_codes[rows[i * s.top_k + j]])[None, :]
+                zs = host(layer.z_scales[rows[i * s.top_k + j]])[None, :]
+                # the GPU's NVFP4 z is exactly the oracle's quantisation of the GPU's bf16 z
+                c_ref, s_ref = oracle.quantize_nvfp4(z_gpu[i, j][None, :], 1.0)
+                assert np.array_equal(zc, c_ref) and np.array_equal(zs, s_ref)
+                a = oracle.dequant_nvfp4_act(zc, zs)[0]
+            else:
+                a = bf16_to_f64(z_gpu[i, j])
+            o_step[i, j] = a @ wd.T
+    o_gpu = bf16_to_f64(o[rows].reshape(len(toks), s.top_k, -1))
+    assert_close_rms(o_gpu, o_step, what="o (down out, step-wise)", ulp_rel=BF16_ULP)
+    assert_close_rms(o_gpu, ref.o, tol=5e-2, what="o (end-to-end)", ulp_rel=BF16_ULP)
+    # combine from the GPU's own o
+    y_step = oracle.combine(o_gpu, topw[toks].astype(np.float64), None if residual is None else residual[toks])
+    assert_close_rms(bf16_to_f64(yb[toks]), bf16_to_f64(y_step), what="y (step-wise)", ulp_rel=BF16_ULP)
+    assert_close_rms(bf16_to_f64(yb[toks]), bf16_to_f64(ref.y), what="y (end-to-end)", ulp_rel=BF16_ULP)
+    return yb, cache
+
+
+def test_tiny_layer_full():
+    w = synth.WORKLOADS["tiny"]
+    W = synth.expert_weights(w)
+    for algo in (moe.MOE_ALGO_AUTO, moe.MOE_ALGO_PREFILL):
+        check_layer(w, 32, W, "mx", "bf16", None, algo=algo)
+
+
+def test_tiny_layer_w4a4_full():
+    w = synth.WORKLOADS["tiny"]
+    W = synth.expert_weights(w)
+    nv = {}
+    for name in ("gate", "up", "down"):
+        sc, g, _ = oracle.transcode_mx_to_nv(W[name][1], W[name][0])
+        nv[name] = (W[name][0], sc, g)
+    check_layer(w, 32, nv, "nv", "nvfp4", None)
+
+
+@pytest.fixture(scope="module")
+def decode_weights():
+    w = synth.WORKLOADS["decode"]
+    W = synth.expert_weights(w)
+    return W, upload_weights(W, "mx"), ExpertCache(W, "mx")
+
+
+@pytest.mark.parametrize("T,sample", [(1, None), (8, [0, 5]), (64, [3, 40, 63])])
+def test_decode_layer(decode_weights, T, sample):
+    W, dw, cache = decode_weights
+    check_layer(synth.WORKLOADS["decode"], T, W, "mx", "bf16", sample, dev_weights=dw, cache=cache)
+
+
+def test_decode_mx_equals_nv_bitwise(decode_weights):
+    """W4A16 on MX weights and on their NV transcode give identical bytes."""
+    W, dw, _ = decode_weights
+    w = synth.WORKLOADS["decode"]
+    s = w.shape
+    nvw = {}
+    for name in ("gate", "up", "down"):
+        t = getattr(dw, name)
+        E, n, kb = t.scale.shape
+        sc, g, cnt = moe.transcode_mx_to_nv(t.scale, t.packed)
+        nvw[name] = moe.Weights(t.packed, sc, g)
+        torch.cuda.synchronize()
+        assert host(cnt)[2] == 0
+    dnv = moe.LayerWeights(nvw["gate"], nvw["up"], nvw["down"])
+    T = 64
+    x = dev_bf16(synth.activations(w, T))
+    l = dev_f32(synth.logits(w, T))
+    outs = []
+    for d in (dw, dnv):
+        layer = moe.MoELayer(d, s.num_experts, s.n_group, s.topk_group, s.top_k, s.routed_scaling_factor, T)
+        outs.append(host_bf16_bits(layer.forward(x, l)).copy())
+    torch.cuda.synchronize()
+    assert np.array_equal(outs[0], outs[1])
+
+
+def test_prefill_layer():
+    w = synth.WORKLOADS["prefill"]
+    W = synth.expert_weights(w)
+    check_layer(w, 8192, W, "mx", "bf16", [0, 4097, 8191])
+
+
+def test_w4a4_layer():
+    w = synth.WORKLOADS["w4a4"]
+    W = synth.expert_weights(w)
+    # the NV weights are the GPU transcode of the MX weights; check it byte-exact first
+    nv = {}
+    for name in ("gate", "up", "down"):
+        packed, mx = W[name]
+        sc, g, cnt = moe.transcode_mx_to_nv(dev_u8(mx), dev_u8(packed))
+        torch.cuda.synchronize()
+        sc_ref, g_ref, cnt_ref = oracle.transcode_mx_to_nv(mx, packed)
+        assert np.array_equal(host(sc), sc_ref)
+        assert np.array_equal(host(g), g_ref)
+        assert list(host(cnt)) == [cnt_ref["blocks"], 0, 0, 0]
+        nv[name] = (packed, sc_ref, g_ref)
+    check_layer(w, 4096, nv, "nv", "nvfp4", [1, 2048, 4095])
+
+
+@pytest.mark.parametrize("amax", synth.OUTLIER_AMAX)
+def test_w4a4_down_outliers(amax):
+    """Down projection alone on N(0,1) inputs with 0.1% outliers (saturation at 2688)."""
+    w = synth.WORKLOADS["w4a4"]
+    s = w.shape
+    rows = 32768
+    z = synth.down_inputs_with_outliers(rows, s.inter, amax)
+    E = s.num_experts
+    offsets = (np.arange(E + 1) * (rows // E)).astype(np.int32)
+    experts = [0, 77, 255]
+    Wd = synth.mx_matrix(2, 0, synth.T_DOWN_CODES, synth.T_DOWN_EXP, E, s.hidden, s.inter)
+    sc, g, _ = oracle.transcode_mx_to_nv(Wd[1], Wd[0])
+    zc, zs = moe.quantize_nvfp4(dev_bf16(z), 1.0)
+    wdev = moe.Weights(dev_u8(Wd[0]), dev_u8(sc), dev_f32(g))
+    o = moe.grouped_gemm(zc, wdev, None, dev_i32_like(offsets), rows, a_scales=zs)
+    torch.cuda.synchronize()
+    c_ref, s_ref = oracle.quantize_nvfp4(z, 1.0)
+    assert np.array_equal(host(zc), c_ref) and np.array_equal(host(zs), s_ref)
+    a = oracle.dequant_nvfp4_act(c_ref, s_ref)
+    assert a.max() == 2688.0 and a.min() == -2688.0
+    ob = bf16_to_f64(host_bf16_bits(o))
+    for e in experts:
+        r = slice(offsets[e], offsets[e] + 24)
+        wd = oracle.dequant_nv(Wd[0][e], sc[e], g[e])
+        assert_close_rms(ob[r], a[r] @ wd.T, what=f"down e={e} amax={amax}", ulp_rel=BF16_ULP)
+
+
+def dev_i32_like(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+def test_reap50_two_layers():
+    w = synth.WORKLOADS["reap50"]
+    T = 16384
+    sample = [0, 9000, 16383]
+    W1 = synth.expert_weights(w, 0)
+    h0 = synth.activations(w, T, 0)
+    y1, _ = check_layer(w, T, W1, "mx", "bf16", sample, layer_idx=0, residual=h0, x=h0)
+    # expert load skew (reported)
+    del W1
+    W2 = synth.expert_weights(w, 1)
+    check_layer(w, T, W2, "mx", "bf16", sample, layer_idx=1, residual=y1, x=y1)
