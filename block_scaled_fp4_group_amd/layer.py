@@ -55,8 +55,15 @@ class MoELayer:
             self.z_scales = torch.empty((R, I // 16), dtype=torch.uint8, device=dev)
 
     def forward(self, x: torch.Tensor, logits: torch.Tensor, bias: Optional[torch.Tensor] = None,
-                residual: Optional[torch.Tensor] = None, algo: int = MOE_ALGO_AUTO, y: Optional[torch.Tensor] = None):
+                residual: Optional[torch.Tensor] = None, algo: int = MOE_ALGO_AUTO, y: Optional[torch.Tensor] = None,
+                events: Optional[dict] = None):
+        """``events``: optional {step name: (start, end)} torch.cuda.Event pairs recorded
+        around the gate/up ("gate_up") and down ("down") GEMM launches."""
         T = x.shape[0]
+
+        def mark(name, i):
+            if events is not None and name in events:
+                events[name][i].record()
         R = T * self.top_k
         ids, topw = self.ids[:T], self.topw[:T]
         route(logits, bias, self.E, self.n_group, self.topk_group, self.top_k, self.scale, True, ids=ids, weights=topw)
@@ -65,16 +72,24 @@ class MoELayer:
         o = self.o[:R]
         if self.act_mode == "nvfp4":
             xc, xs = quantize_nvfp4(x, self.input_scale, self.x_codes[:T], self.x_scales[:T])
+            mark("gate_up", 0)
             grouped_gemm(xc, self.w.gate, self.w.up, self.offsets, R, gather=self.sorted_slots[:R],
                          gather_div=self.top_k, a_scales=xs, input_scale=self.input_scale, out=z,
                          out_codes=self.z_codes[:R], out_scales=self.z_scales[:R], output_scale=self.input_scale,
                          want_bf16=z is not None, algo=algo)
+            mark("gate_up", 1)
+            mark("down", 0)
             grouped_gemm(self.z_codes[:R], self.w.down, None, self.offsets, R, a_scales=self.z_scales[:R],
                          input_scale=self.input_scale, out=o, algo=algo)
+            mark("down", 1)
         else:
+            mark("gate_up", 0)
             grouped_gemm(x, self.w.gate, self.w.up, self.offsets, R, gather=self.sorted_slots[:R],
                          gather_div=self.top_k, out=z, algo=algo)
+            mark("gate_up", 1)
+            mark("down", 0)
             grouped_gemm(z, self.w.down, None, self.offsets, R, out=o, algo=algo)
+            mark("down", 1)
         y = self.y[:T] if y is None else y
         combine(o, self.slot_rows[:R], topw, residual, y=y)
         return y
