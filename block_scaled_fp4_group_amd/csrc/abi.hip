@@ -149,6 +149,11 @@ moe_status moe_fp4_grouped_gemm(const moe_act* a, const moe_fp4_weights* w0, con
     MOE_CHECK(is_pow2_float(a->input_scale), "moe_fp4_grouped_gemm: input_scale must be a power of two");
   }
   if (a->gather) MOE_CHECK(a->gather_div >= 1, "moe_fp4_grouped_gemm: gather_div < 1");
+  MOE_CHECK(a->rows_src >= 0, "moe_fp4_grouped_gemm: rows_src < 0");
+  if (a->rows_src * (int64_t)w0->k * 2 >= ((int64_t)1 << 31)) {
+    set_error("moe_fp4_grouped_gemm: activations larger than 2 GiB are not supported");
+    return MOE_ERR_UNSUPPORTED;
+  }
   MOE_CHECK(out->data || out->codes, "moe_fp4_grouped_gemm: no output");
   if (out->data) MOE_CHECK(aligned16(out->data), "moe_fp4_grouped_gemm: output not 16-byte aligned");
   if (out->codes) {
@@ -164,6 +169,7 @@ moe_status moe_fp4_grouped_gemm(const moe_act* a, const moe_fp4_weights* w0, con
   g.a_scales = a->scales;
   g.a_gscale = a->mode == MOE_ACT_NVFP4 ? a->input_scale : 1.0f;
   g.gather = a->gather;
+  g.a_bytes = a->rows_src * (a->mode == MOE_ACT_NVFP4 ? (int64_t)(w0->k / 2) : (int64_t)w0->k * 2);
   g.gather_div = a->gather ? a->gather_div : 1;
   g.w_packed[0] = w0->packed;
   g.w_scale[0] = w0->scale;

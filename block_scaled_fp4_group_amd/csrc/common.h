@@ -37,19 +37,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // --------------------------------------------------------- scale decoders
 // E8M0 byte -> float 2^(b-127); 0xFF -> NaN; 0x00 -> 2^-127 (a float subnormal).
 __device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
-  if (b == 0xFFu) return __uint_as_float(0x7FC00000u);
-  if (b == 0u) return __uint_as_float(0x00400000u);
-  return __uint_as_float(b << 23);
+  uint32_t u = b << 23;
+  u = (b == 0u) ? 0x00400000u : u;        // selects, no branches
+  u = (b == 0xFFu) ? 0x7FC00000u : u;
+  return __uint_as_float(u);
 }
 
 // E4M3 (FN) byte -> float (exact).  0x7F / 0xFF -> NaN.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
   uint32_t e = (b >> 3) & 0xFu, m = b & 7u;
-  float mag;
-  if ((b & 0x7Fu) == 0x7Fu) mag = __uint_as_float(0x7FC00000u);
-  else if (e == 0) mag = (float)m * 0.001953125f;                  // m * 2^-9
-  else mag = __uint_as_float(((e + 120u) << 23) | (m << 20));
-  return (b & 0x80u) ? -mag : mag;
+  float normal = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  float sub = (float)m * 0.001953125f;                              // m * 2^-9
+  float mag = (e == 0) ? sub : normal;                              // selects, no branches
+  mag = ((b & 0x7Fu) == 0x7Fu) ? __uint_as_float(0x7FC00000u) : mag;
+  return __uint_as_float(__float_as_uint(mag) | ((b & 0x80u) << 24));
 }
 
 __device__ __forceinline__ bool is_pow2_scale(float s) {
@@ -94,6 +95,25 @@ __device__ __forceinline__ bf16x8 fp4x8_to_bf16_general(uint32_t codes, float sc
 __device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t codes, float scale) {
   if (is_pow2_scale(scale)) return fp4x8_to_bf16_pow2(codes, scale);
   return fp4x8_to_bf16_general(codes, scale);
+}
+
+// ---------------------------------------------------------- buffer loads
+// Raw buffer descriptor over [base, base + bytes): loads whose offset falls
+// outside the range return zero and touch no memory (hardware range check).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload128(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ uint32_t bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ uint32_t bload8(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
 }
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {

@@ -11,6 +11,7 @@ struct GemmArgs {
   float a_gscale;                 // NVFP4 global scale (power of two)
   const int32_t* gather;          // permuted row r reads source row gather[r] / gather_div
   int gather_div;
+  int64_t a_bytes;                // bytes of a_data (bf16 rows or NVFP4 codes)
   // weights [E, N, K]: codes [E, N, K/2]; MX E8M0 [E, N, K/32] | NV E4M3 [E, N, K/16] + float [E]
   const uint8_t* w_packed[2];
   const uint8_t* w_scale[2];

@@ -334,3 +334,45 @@ def test_grouped_gemm_empty_and_invalid():
         moe.grouped_gemm(x, wg, wg, offsets, 4, out=out, input_scale=3.0,
                          a_scales=torch.zeros((4, H // 16), dtype=torch.uint8, device="cuda"))
     assert ei.value.status == moe.MOE_ERR_INVALID
+
+
+@pytest.mark.parametrize("algo", [moe.MOE_ALGO_DECODE, moe.MOE_ALGO_PREFILL])
+@pytest.mark.parametrize("fmt", ["mx", "nv"])
+@pytest.mark.parametrize("amode", ["bf16", "nvfp4"])
+def test_grouped_gemm_model_k(algo, fmt, amode):
+    """The model's K (4096 for gate/up, 2048 for down) with ragged expert loads."""
+    E, H, I = 4, 4096, 256
+    counts = np.array([3, 0, 21, 40])
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offsets[-1])
+    say(f"gemm model-K algo={algo} fmt={fmt} amode={amode} R={R}")
+    x = synth.random_bf16(71, (40, H))
+    gather = np.random.default_rng(72).integers(0, 40 * 8, size=R).astype(np.int32)
+    wg, dg = _gemm_problem(73, E, I, H, counts, 40, fmt)
+    wu, du = _gemm_problem(74, E, I, H, counts, 40, fmt)
+    wd, dd = _gemm_problem(75, E, 512, 2048, counts, R, fmt)
+    if amode == "nvfp4":
+        xc, xs = oracle.quantize_nvfp4(x, 1.0)
+        a_val, a_dev, a_sc = oracle.dequant_nvfp4_act(xc, xs), dev_u8(xc), dev_u8(xs)
+    else:
+        a_val, a_dev, a_sc = bf16_to_f64(x), dev_bf16(x), None
+    z = moe.grouped_gemm(a_dev, wg, wu, dev_i32(offsets), R, gather=dev_i32(gather), gather_div=8, a_scales=a_sc,
+                         algo=algo)
+    z2 = synth.random_bf16(76, (R, 2048))
+    if amode == "nvfp4":
+        zc, zs = oracle.quantize_nvfp4(z2, 1.0)
+        z_val, z_dev, z_sc = oracle.dequant_nvfp4_act(zc, zs), dev_u8(zc), dev_u8(zs)
+    else:
+        z_val, z_dev, z_sc = bf16_to_f64(z2), dev_bf16(z2), None
+    o = moe.grouped_gemm(z_dev, wd, None, dev_i32(offsets), R, a_scales=z_sc, algo=algo)
+    torch.cuda.synchronize()
+    zref = np.zeros((R, I))
+    oref = np.zeros((R, 512))
+    for e in range(E):
+        rows = slice(offsets[e], offsets[e + 1])
+        a = a_val[gather[rows] // 8]
+        zref[rows] = oracle.silu(a @ dg[e].T) * (a @ du[e].T)
+        oref[rows] = z_val[rows] @ dd[e].T
+    zref = bf16_to_f64(oracle.round_to_bf16_bits(zref))
+    assert_close_rms(bf16_to_f64(host_bf16_bits(z)), zref, what="z", ulp_rel=BF16_ULP)
+    assert_close_rms(bf16_to_f64(host_bf16_bits(o)), oref, what="o", ulp_rel=BF16_ULP)
