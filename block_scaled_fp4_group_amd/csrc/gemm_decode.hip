@@ -246,7 +246,7 @@ __device__ __forceinline__ void stage_rows(const GemmArgs& p, uint8_t* lds, int 
 #define MOE_DEC_MR_4096 8
 #endif
 #ifndef MOE_DEC_MR_2048
-#define MOE_DEC_MR_2048 16
+#define MOE_DEC_MR_2048 8
 #endif
 #ifndef MOE_DEC_PF2
 #define MOE_DEC_PF2 8
