@@ -8,8 +8,16 @@
 // lower-index tie-breaks, normalisation) are documented in moe_fp4.h.
 //
 // Lane l of the wave owns experts l, l+64, l+128, l+192 (E <= 256), so every
-// load of the logits row is coalesced.  Group scores live in LDS; each
-// selection round is a wave-wide argmax by shuffles over (value, index) pairs.
+// load of the logits row is coalesced.  The reductions run in registers:
+// within a row of 16 lanes with DPP moves (quad permutes, half-row and row
+// mirrors), across rows with the gfx950 16- and 32-lane swaps, so a wave-wide
+// argmax costs a few dozen cycles per level instead of an LDS round trip.
+//   * group score (sum of the two largest biased scores): a segmented top-2
+//     merge over the group's lanes when the group size is a power of two, an
+//     LDS scan otherwise;
+//   * kept groups: every lane ranks the group scores (ties to the lower index);
+//   * experts: top_k rounds of a wave argmax over (score, index), ties to the
+//     lower index.
 #include "common.h"
 
 namespace moe {
@@ -17,15 +25,78 @@ namespace moe {
 constexpr int kRouteMaxPer = 4;        // experts per lane, E <= 256
 constexpr int kRouteWaves = 4;         // tokens per 256-thread block
 
+// ---- cross-lane moves of 32- and 64-bit values
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int x) {
+  return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xF, 0xF, false);
+}
+// partner across the 16-lane row pair (l ^ 16) and across the wave halves (l ^ 32)
+__device__ __forceinline__ int swap16_i32(int x) {
+  auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return (threadIdx.x & 16) ? r[0] : r[1];
+}
+__device__ __forceinline__ int swap32_i32(int x) {
+  auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return (threadIdx.x & 32) ? r[0] : r[1];
+}
+// level L of a butterfly over aligned groups of 2^(L+1) lanes: the partner is
+// always in the other half of the group (quad permutes, then the half-row and
+// row mirrors, then the swaps)
+template <int L>
+__device__ __forceinline__ int partner_i32(int x) {
+  if constexpr (L == 0) return dpp_i32<0xB1>(x);        // quad_perm [1,0,3,2]
+  else if constexpr (L == 1) return dpp_i32<0x4E>(x);   // quad_perm [2,3,0,1]
+  else if constexpr (L == 2) return dpp_i32<0x141>(x);  // row_half_mirror
+  else if constexpr (L == 3) return dpp_i32<0x140>(x);  // row_mirror
+  else if constexpr (L == 4) return swap16_i32(x);
+  else return swap32_i32(x);
+}
+template <int L>
+__device__ __forceinline__ double partner_f64(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)partner_i32<L>((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)partner_i32<L>((int)(uint32_t)(u >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// ---- (value, index) argmax: larger value wins, equal values go to the lower
+// index, index -1 is empty
+__device__ __forceinline__ void argmax_merge(double& v, int& i, double ov, int oi) {
+  const bool take = (oi >= 0) && (i < 0 || ov > v || (ov == v && oi < i));
+  v = take ? ov : v;
+  i = take ? oi : i;
+}
+template <int L>
+__device__ __forceinline__ void argmax_level(double& v, int& i) {
+  argmax_merge(v, i, partner_f64<L>(v), partner_i32<L>(i));
+}
 __device__ __forceinline__ void wave_argmax(double& v, int& i) {
-  // maximise v; on equal v keep the lower index; index -1 means "empty"
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    double ov = __shfl_xor(v, off, kWave);
-    int oi = __shfl_xor(i, off, kWave);
-    bool take = (oi >= 0) && (i < 0 || ov > v || (ov == v && oi < i));
-    if (take) { v = ov; i = oi; }
-  }
+  argmax_level<0>(v, i);
+  argmax_level<1>(v, i);
+  argmax_level<2>(v, i);
+  argmax_level<3>(v, i);
+  argmax_level<4>(v, i);
+  argmax_level<5>(v, i);
+}
+
+// ---- top-2 of a multiset as (b1 >= b2); merging two disjoint halves
+__device__ __forceinline__ void top2_merge(double& b1, double& b2, double o1, double o2) {
+  const double n2 = (b1 >= o1) ? fmax(b2, o1) : fmax(b1, o2);
+  b1 = fmax(b1, o1);
+  b2 = n2;
+}
+template <int L>
+__device__ __forceinline__ void top2_level(double& b1, double& b2) {
+  top2_merge(b1, b2, partner_f64<L>(b1), partner_f64<L>(b2));
+}
+// segmented over aligned groups of 2^levels lanes
+__device__ __forceinline__ void top2_segment(double& b1, double& b2, int levels) {
+  if (levels > 0) top2_level<0>(b1, b2);
+  if (levels > 1) top2_level<1>(b1, b2);
+  if (levels > 2) top2_level<2>(b1, b2);
+  if (levels > 3) top2_level<3>(b1, b2);
+  if (levels > 4) top2_level<4>(b1, b2);
+  if (levels > 5) top2_level<5>(b1, b2);
 }
 
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits,
@@ -41,83 +112,114 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   const bool valid = t0 < T;           // no early exit: the block synchronises below
   const int64_t t = valid ? t0 : T - 1;
   const int gs = E / n_group;
+  const bool pow2 = (gs & (gs - 1)) == 0;
   const float* lrow = logits + t * E;
 
   double s[kRouteMaxPer], c[kRouteMaxPer];
 #pragma unroll
   for (int j = 0; j < kRouteMaxPer; ++j) {
-    int e = lane + 64 * j;
+    const int e = lane + 64 * j;
     if (e < E) {
-      double l = (double)lrow[e];
+      const double l = (double)lrow[e];
       s[j] = 1.0 / (1.0 + exp(-l));
       c[j] = s[j] + (bias ? (double)bias[e] : 0.0);
-      cval[wv][e] = c[j];
     } else {
       s[j] = 0.0;
-      c[j] = 0.0;
+      c[j] = -INFINITY;
+    }
+  }
+
+  // ---- group scores -> gscore[wv][g]
+  if (pow2) {
+    const int levels = 31 - __clz(min(gs, 64));
+    double p1[kRouteMaxPer], p2[kRouteMaxPer];
+#pragma unroll
+    for (int j = 0; j < kRouteMaxPer; ++j) {
+      p1[j] = c[j];
+      p2[j] = -INFINITY;
+      top2_segment(p1[j], p2[j], levels);
+    }
+    if (gs <= 64) {
+      // lane l heads the group of experts l + 64j .. l + 64j + gs - 1
+      if ((lane & (gs - 1)) == 0) {
+#pragma unroll
+        for (int j = 0; j < kRouteMaxPer; ++j)
+          if (lane + 64 * j < E) gscore[wv][(lane + 64 * j) / gs] = p1[j] + p2[j];
+      }
+    } else if (lane == 0) {
+      // a group spans gs / 64 rows of the wave: merge them in order
+      for (int g = 0; g < n_group; ++g) {
+        double b1 = -INFINITY, b2 = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kRouteMaxPer; ++j)
+          if ((64 * j) / gs == g && 64 * j < E) top2_merge(b1, b2, p1[j], p2[j]);
+        gscore[wv][g] = b1 + b2;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kRouteMaxPer; ++j)
+      if (lane + 64 * j < E) cval[wv][lane + 64 * j] = c[j];
+    __syncthreads();
+    if (lane < n_group) {
+      double b1 = -INFINITY, b2 = -INFINITY;
+      for (int e = lane * gs; e < (lane + 1) * gs; ++e) {
+        const double v = cval[wv][e];
+        if (v > b1) { b2 = b1; b1 = v; }
+        else if (v > b2) { b2 = v; }
+      }
+      gscore[wv][lane] = b1 + b2;
     }
   }
   __syncthreads();
 
-  // group score: sum of the two largest c in the group (lane g scans group g)
+  // ---- keep the topk_group best groups: lane g ranks group g
+  bool keep = false;
   if (lane < n_group) {
-    double b1 = -INFINITY, b2 = -INFINITY;
-    for (int e = lane * gs; e < (lane + 1) * gs; ++e) {
-      double v = cval[wv][e];
-      if (v > b1) { b2 = b1; b1 = v; }
-      else if (v > b2) { b2 = v; }
+    const double mine = gscore[wv][lane];
+    int rank = 0;
+    for (int g = 0; g < n_group; ++g) {
+      const double o = gscore[wv][g];
+      rank += (o > mine || (o == mine && g < lane)) ? 1 : 0;
     }
-    gscore[wv][lane] = b1 + b2;
+    keep = rank < topk_group;
   }
-  __syncthreads();
+  const uint64_t kept = __ballot(keep);
 
-  // keep topk_group groups: repeated wave argmax over the group scores
-  uint64_t kept = 0;   // bit g set when group g is kept
-  for (int r = 0; r < topk_group; ++r) {
-    double v = -INFINITY;
-    int i = -1;
-    if (lane < n_group && !((kept >> lane) & 1ull)) { v = gscore[wv][lane]; i = lane; }
-    wave_argmax(v, i);
-    kept |= 1ull << i;
-  }
-
-  // top_k experts among kept groups
-  bool taken[kRouteMaxPer];
+  // ---- top_k experts among the kept groups
   bool elig[kRouteMaxPer];
 #pragma unroll
   for (int j = 0; j < kRouteMaxPer; ++j) {
-    int e = lane + 64 * j;
-    taken[j] = false;
+    const int e = lane + 64 * j;
     elig[j] = (e < E) && ((kept >> (e / gs)) & 1ull);
   }
-  double sel_s = 0.0;    // lane r < top_k keeps the r-th pick's score
+  double sel_s = 0.0, tot = 0.0;     // lane r < top_k keeps the r-th pick
   int sel_e = 0;
   for (int r = 0; r < top_k; ++r) {
     double v = -INFINITY;
     int i = -1;
 #pragma unroll
-    for (int j = 0; j < kRouteMaxPer; ++j) {
-      int e = lane + 64 * j;
-      if (elig[j] && !taken[j] && (i < 0 || c[j] > v)) { v = c[j]; i = e; }
-    }
-    wave_argmax(v, i);
-#pragma unroll
     for (int j = 0; j < kRouteMaxPer; ++j)
-      if (lane + 64 * j == i) taken[j] = true;
-    // the owner broadcasts the unbiased score of the pick
+      if (elig[j] && (i < 0 || c[j] > v)) { v = c[j]; i = lane + 64 * j; }
+    wave_argmax(v, i);
+    // every lane now holds the pick; its owner supplies the unbiased score
+    const int pick = __builtin_amdgcn_readfirstlane(i);
     double sv = 0.0;
 #pragma unroll
-    for (int j = 0; j < kRouteMaxPer; ++j)
-      if (lane + 64 * j == i) sv = s[j];
-    int owner = i & 63;
-    sv = __shfl(sv, owner, kWave);
-    if (lane == r) { sel_s = sv; sel_e = i; }
+    for (int j = 0; j < kRouteMaxPer; ++j) {
+      const bool mine = lane + 64 * j == pick;
+      sv = mine ? s[j] : sv;
+      elig[j] = elig[j] && !mine;
+    }
+    const uint64_t su = (uint64_t)__double_as_longlong(sv);
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)su, pick & 63);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(su >> 32), pick & 63);
+    sv = __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+    tot += sv;                                     // sum in pick order
+    if (lane == r) { sel_s = sv; sel_e = pick; }
   }
-  // weights: normalise over the picks (sum in pick order), scale
-  double tot = 0.0;
-  for (int r = 0; r < top_k; ++r) tot += __shfl(sel_s, r, kWave);
   if (valid && lane < top_k) {
-    double w = norm ? sel_s / tot * (double)scale : sel_s * (double)scale;
+    const double w = norm ? sel_s / tot * (double)scale : sel_s * (double)scale;
     ids[t * top_k + lane] = sel_e;
     weights[t * top_k + lane] = (float)w;
   }
