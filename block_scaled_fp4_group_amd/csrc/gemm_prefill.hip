@@ -8,16 +8,22 @@
 //   * a workgroup of 8 waves owns a tile of BM = 128 token rows x BN = 256
 //     weight rows (SwiGLU: 128 gate + 128 up rows of the same outputs) and
 //     walks K in steps of BK = 128;
-//   * the token tile is gathered from HBM/L2 into registers one step ahead and
-//     written to a double-buffered LDS stage with an XOR swizzle (16-byte
-//     chunk c of row r sits at c ^ (r % 16)), so the 16 rows of one MFMA
-//     operand read hit 16 distinct bank groups; NVFP4 token rows are
-//     dequantised to bf16 on the way in;
-//   * each wave keeps its 64 weight rows' FP4 codes in registers (one step
-//     ahead), dequantises them with the gfx950 convert instruction and runs
-//     4 x 4 bf16 16x16x32 MFMA tiles (64 tokens x 64 weight rows);
-//   * persistent workgroups walk the tiles expert by expert, the m-tiles of one
-//     (expert, n-tile) back to back so their weights are shared in cache.
+//   * every step's operands -- the gathered token rows (bf16, or NVFP4
+//     dequantised on the way in), the weight rows' FP4 codes and their scales --
+//     are fetched cooperatively two steps ahead into registers and written to
+//     one of two LDS stages one step ahead, so a load has two steps of MFMA
+//     work to arrive; the step loop is unrolled by two so every register set
+//     and stage is static;
+//   * LDS layouts are XOR-swizzled so the MFMA operand reads are conflict
+//     free: token chunk c (16 B) of row r at c ^ (r % 16) in a 256-B row,
+//     weight chunk c of row n at c ^ ((n / 2) % 4) in a 64-B row;
+//   * each wave dequantises its 64 weight rows from LDS with the gfx950
+//     convert instruction and runs 4 x 4 bf16 16x16x32 MFMA tiles (64 tokens
+//     x 64 weight rows);
+//   * persistent workgroups: the tile list, ordered (expert, n-tile, m-tile),
+//     is cut into one contiguous slice per XCD (workgroup b runs on XCD b % 8),
+//     so the workgroups sharing an L2 work on the same experts' token rows and
+//     weight slices at the same time.
 #include <algorithm>
 
 #include "gemm_common.h"
@@ -25,11 +31,16 @@
 namespace moe {
 
 constexpr int kPfBM = 128, kPfBN = 256, kPfBK = 128;
-constexpr int kPfThreads = 512;                    // 8 waves: 2 along tokens x 4 along weight rows
-constexpr int kPfStage = kPfBM * kPfBK * 2;        // 32 KB of bf16 per LDS stage
+constexpr int kPfThreads = 512;                          // 8 waves: 2 along tokens x 4 along weight rows
+constexpr int kPfAStage = kPfBM * kPfBK * 2;             // 32 KB of bf16 tokens
+constexpr int kPfWStage = kPfBN * kPfBK / 2;             // 16 KB of FP4 codes
+constexpr int kPfSStage = kPfBN * 8;                     // 2 KB of scales (MX uses 4 B per row)
+constexpr int kPfStage = kPfAStage + kPfWStage + kPfSStage;
 constexpr int kPfMaxE = 1024;
+constexpr int kPfXcds = 8;
 
-__device__ __forceinline__ uint32_t swz(int row, int chunk) { return (uint32_t)(row * 256 + ((chunk ^ (row & 15)) << 4)); }
+__device__ __forceinline__ uint32_t swz_a(int row, int chunk) { return (uint32_t)(row * 256 + ((chunk ^ (row & 15)) << 4)); }
+__device__ __forceinline__ uint32_t swz_w(int row, int chunk) { return (uint32_t)(row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4)); }
 
 __device__ __forceinline__ uint32_t quant4_lanes(const float* v, float inv_g, uint32_t& sb_out) {
   float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
@@ -50,24 +61,34 @@ __device__ __forceinline__ uint32_t quant4_lanes(const float* v, float inv_g, ui
   return bits;
 }
 
+// registers of one step in flight (per thread)
+template <bool A_NV>
+struct PfRegs {
+  u32x4 a[A_NV ? 1 : 4];   // bf16: 4 token chunks; NVFP4: 32 codes
+  uint32_t asc;            // NVFP4: the two E4M3 scales of those codes
+  u32x4 w[2];              // 2 weight-code chunks
+  uint32_t s;              // one dword of weight scales
+};
+
 template <int NMAT, bool W_NV, bool A_NV>
 __global__ __launch_bounds__(kPfThreads) void gemm_prefill_kernel(GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];      // 2 stages
   __shared__ int s_pref[kPfMaxE + 1];                                // tiles before expert e
   __shared__ int s_wc[kPfThreads / kWave];
 
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
   const int wm = wv & 1, wn = wv >> 1;                               // 2 x 4 waves
   const int li = lane & 15, lg = lane >> 4;
   const int E = p.E, K = p.K, N = p.N;
   const int ntn = N / (kPfBN / NMAT);                                // n-tiles per expert
-  const int nk = K / kPfBK;
+  const int nk = K / kPfBK;                                          // even (checked on the host)
 
   // ---- tile table: expert e owns ceil(rows_e / BM) * ntn tiles
   {
     int running = 0;
     for (int e0 = 0; e0 < E; e0 += kPfThreads) {
-      const int e = e0 + threadIdx.x;
+      const int e = e0 + tid;
       int cnt = 0;
       if (e < E) {
         int r0 = (int)max((int64_t)0, min((int64_t)p.offsets[e], p.rows));
@@ -90,16 +111,28 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_kernel(GemmArgs p) {
       running += tot;
       __syncthreads();
     }
-    if (threadIdx.x == 0) s_pref[E] = running;
+    if (tid == 0) s_pref[E] = running;
     __syncthreads();
   }
   const int total = s_pref[E];
 
+  // ---- this workgroup's share: a contiguous slice of the tile list per XCD
+  const int nx = (gridDim.x % kPfXcds == 0) ? kPfXcds : 1;
+  const int xcd = blockIdx.x % nx, per = gridDim.x / nx, slot = blockIdx.x / nx;
+  const int t_begin = (int)((int64_t)total * xcd / nx), t_end = (int)((int64_t)total * (xcd + 1) / nx);
+
   const uint32_t sc_row = (uint32_t)(W_NV ? K / 16 : K / 32);
   const uint32_t mat_codes = (uint32_t)N * (uint32_t)(K / 2);
   const uint32_t mat_scales = (uint32_t)N * sc_row;
+  const rsrc_t ar = make_rsrc(p.a_data, (uint32_t)p.a_bytes);
+  const rsrc_t asr = make_rsrc(A_NV ? p.a_scales : p.a_data, A_NV ? (uint32_t)(p.a_bytes / 8) : 0u);
 
-  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+  // block-local weight row n (0..255) -> row within its matrix's slab (matrix n / 128 for SwiGLU)
+  auto wrow = [&](int n) { return NMAT == 2 ? (n & 127) : n; };
+  // this wave's weight group g (16 rows): block-local row base
+  auto lrow = [&](int g) { return NMAT == 2 ? (g >> 1) * 128 + wn * 32 + (g & 1) * 16 : wn * 64 + g * 16; };
+
+  for (int tile = t_begin + slot; tile < t_end; tile += per) {
     // ---- locate (expert, n-tile, m-tile); m-tiles of one n-tile are consecutive
     int lo = 0, hi = E - 1;
     while (lo < hi) {
@@ -115,88 +148,86 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_kernel(GemmArgs p) {
     const int nt = local / mt_cnt, mt = local % mt_cnt;
     const int rbase = r0 + mt * kPfBM;
     const int mrows = min(kPfBM, r1 - rbase);
+    const int nbase = nt * (kPfBN / NMAT);                           // first row of each matrix's slab
 
-    // ---- weight rows of this wave (4 groups of 16)
     rsrc_t wr[NMAT], sr[NMAT];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
       wr[m] = make_rsrc(p.w_packed[m] + (int64_t)e * mat_codes, mat_codes);
       sr[m] = make_rsrc(p.w_scale[m] + (int64_t)e * mat_scales, mat_scales);
     }
-    // row group g: matrix mat(g), row wrow(g) + li
-    auto gmat = [&](int g) { return NMAT == 2 ? (g >> 1) : 0; };
-    auto grow = [&](int g) {
-      return NMAT == 2 ? nt * 128 + wn * 32 + (g & 1) * 16 : nt * 256 + wn * 64 + g * 16;
-    };
-    uint32_t wo[4], so[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      wo[g] = (uint32_t)(grow(g) + li) * (uint32_t)(K / 2) + (uint32_t)lg * 16u;
-      so[g] = (uint32_t)(grow(g) + li) * sc_row + (uint32_t)(W_NV ? lg * 2 : lg);
-    }
     float wglob[NMAT];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) wglob[m] = W_NV ? p.w_global[m][e] : 1.0f;
 
-    // ---- token tile loader: thread -> (row, 16-byte chunk) slots
-    // bf16: 4 chunks per thread; NVFP4: one 32-value block per thread
-    int64_t tsrc[4];
-    int trow[4];
+    // ---- what this thread fetches each step
+    // tokens: bf16 -> chunks q = tid + 512 j (row q / 16, chunk q % 16); NVFP4 -> row tid / 4, 32 codes (tid % 4)
+    uint32_t a_off[A_NV ? 1 : 4];
+    uint32_t as_off = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int q = A_NV ? (int)threadIdx.x : (int)threadIdx.x + kPfThreads * j;
-      const int row = A_NV ? q / 4 : q / 16;
-      trow[j] = row;
-      tsrc[j] = -1;
-      if (row < mrows && (!A_NV || j == 0)) {
-        const int64_t r = rbase + row;
-        tsrc[j] = p.gather ? (int64_t)(p.gather[r] / p.gather_div) : r;
+    for (int j = 0; j < (A_NV ? 1 : 4); ++j) {
+      const int q = tid + kPfThreads * j;
+      const int row = A_NV ? (q >> 2) : (q >> 4);
+      const int64_t r = rbase + min(row, mrows - 1);                 // rows past the tile's end reread a valid row
+      const int64_t src = p.gather ? (int64_t)(p.gather[r] / p.gather_div) : r;
+      if (A_NV) {
+        a_off[j] = (uint32_t)(src * (K / 2)) + (uint32_t)(q & 3) * 16u;
+        as_off = (uint32_t)(src * (K / 16)) + (uint32_t)(q & 3) * 2u;
+      } else {
+        a_off[j] = (uint32_t)(src * (int64_t)K * 2) + (uint32_t)(q & 15) * 16u;
       }
     }
-    u32x4 treg[4];
-    uint32_t tsc = 0;
-    auto tload = [&](int kb) {
+    // weight codes: chunks q = tid + 512 j (row q / 4, chunk q % 4); scales: MX row tid (tid < 256), NV row tid / 2, half tid % 2
+    uint32_t w_off[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int q = tid + kPfThreads * j;
+      w_off[j] = (uint32_t)(nbase + wrow(q >> 2)) * (uint32_t)(K / 2) + (uint32_t)(q & 3) * 16u;
+    }
+    const int s_n = W_NV ? (tid >> 1) : (tid & 255);
+    const uint32_t s_off = (uint32_t)(nbase + wrow(s_n)) * sc_row + (W_NV ? (uint32_t)(tid & 1) * 4u : 0u);
+    // the matrix of a load is uniform per wave: code chunk j of any thread is in
+    // matrix j (SwiGLU), a scale dword of wave w in matrix (w / 4) (NV) or (w / 2) % 2 (MX)
+    const int wvu = __builtin_amdgcn_readfirstlane(wv);
+    const int smat = NMAT == 2 ? (W_NV ? (wvu >> 2) : ((wvu >> 1) & 1)) : 0;
+    const rsrc_t s_rsrc = smat == 0 ? sr[0] : sr[NMAT - 1];
+
+    auto fetch = [&](PfRegs<A_NV>& R, int kb) {
       if (A_NV) {
-        const int b = threadIdx.x & 3;                               // block within BK
-        if (tsrc[0] >= 0) {
-          treg[0] = *(const u32x4*)(p.a_data + tsrc[0] * (K / 2) + (int64_t)(kb * 4 + b) * 16);
-          tsc = *(const uint16_t*)(p.a_scales + tsrc[0] * (K / 16) + (int64_t)(kb * 4 + b) * 2);
-        }
+        R.a[0] = bload128(ar, a_off[0] + (uint32_t)kb * 64u, 0);
+        R.asc = bload16(asr, as_off + (uint32_t)kb * 8u, 0);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) R.a[j] = bload128(ar, a_off[j] + (uint32_t)kb * 256u, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) R.w[j] = bload128(wr[NMAT == 2 ? j : 0], w_off[j] + (uint32_t)kb * 64u, 0);
+      R.s = bload32(s_rsrc, s_off + (uint32_t)kb * (W_NV ? 8u : 4u), 0);
+    };
+    auto store = [&](const PfRegs<A_NV>& R, uint8_t* st) {
+      uint8_t* sa = st;
+      uint8_t* sw = st + kPfAStage;
+      uint8_t* ss = st + kPfAStage + kPfWStage;
+      if (A_NV) {
+        const int row = tid >> 2, c = tid & 3;
+        const float s_lo = e4m3_to_f32(R.asc & 0xFF) * p.a_gscale, s_hi = e4m3_to_f32((R.asc >> 8) & 0xFF) * p.a_gscale;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          *(u32x4*)(sa + swz_a(row, c * 4 + s)) = __builtin_bit_cast(u32x4, fp4x8_to_bf16(R.a[0][s], s < 2 ? s_lo : s_hi));
       } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int c = (threadIdx.x + kPfThreads * j) & 15;
-          if (tsrc[j] >= 0) treg[j] = *(const u32x4*)(p.a_data + tsrc[j] * (int64_t)K * 2 + (int64_t)kb * 256 + c * 16);
+          const int q = tid + kPfThreads * j;
+          *(u32x4*)(sa + swz_a(q >> 4, q & 15)) = R.a[j];
         }
       }
-    };
-    auto tstore = [&](uint8_t* stage) {
-      if (A_NV) {
-        if (tsrc[0] >= 0) {
-          const int b = threadIdx.x & 3;
-          const float s_lo = e4m3_to_f32(tsc & 0xFF) * p.a_gscale, s_hi = e4m3_to_f32(tsc >> 8) * p.a_gscale;
 #pragma unroll
-          for (int s = 0; s < 4; ++s)
-            *(u32x4*)(stage + swz(trow[0], b * 4 + s)) =
-                __builtin_bit_cast(u32x4, fp4x8_to_bf16(treg[0][s], s < 2 ? s_lo : s_hi));
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int c = (threadIdx.x + kPfThreads * j) & 15;
-          if (tsrc[j] >= 0) *(u32x4*)(stage + swz(trow[j], c)) = treg[j];
-        }
+      for (int j = 0; j < 2; ++j) {
+        const int q = tid + kPfThreads * j;
+        *(u32x4*)(sw + swz_w(q >> 2, q & 3)) = R.w[j];
       }
-    };
-    // ---- weights one step ahead
-    u32x4 wreg[2][4];
-    uint32_t sreg[2][4];
-    auto wload = [&](int buf, int kb) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        wreg[buf][g] = bload128(wr[gmat(g)], wo[g] + kb * 64, 0);
-        sreg[buf][g] = W_NV ? bload16(sr[gmat(g)], so[g] + kb * 8, 0) : bload8(sr[gmat(g)], so[g] + kb * 4, 0);
-      }
+      // NV: row tid / 2, half tid % 2; MX: row tid (threads >= 256 write an unread copy)
+      *(uint32_t*)(ss + tid * 4) = R.s;
     };
 
     f32x4 acc[4][4];                                                 // [weight group][token group]
@@ -205,47 +236,64 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_kernel(GemmArgs p) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    __syncthreads();                                                 // previous tile done with LDS
-    tload(0);
-    wload(0, 0);
-    tstore(lds);
-    __syncthreads();
-
-    for (int kb = 0; kb < nk; ++kb) {
-      const int cur = kb & 1;
-      uint8_t* stage = lds + cur * kPfStage;
-      if (kb + 1 < nk) {
-        tload(kb + 1);
-        wload(cur ^ 1, kb + 1);
-      }
-      // ---- 4 k-slots of 8 values inside this lane group's block
+    auto compute = [&](const uint8_t* st) {
+      const uint8_t* sa = st;
+      const uint8_t* sw = st + kPfAStage;
+      const uint8_t* ss = st + kPfAStage + kPfWStage;
+      u32x4 wq[4];
       float s_lo[4], s_hi[4];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
+        const int n = lrow(g) + li;
+        wq[g] = *(const u32x4*)(sw + swz_w(n, lg));
         if (W_NV) {
-          s_lo[g] = e4m3_to_f32(sreg[cur][g] & 0xFF);
-          s_hi[g] = e4m3_to_f32((sreg[cur][g] >> 8) & 0xFF);
+          const uint32_t b2 = *(const uint16_t*)(ss + n * 8 + lg * 2);
+          s_lo[g] = e4m3_to_f32(b2 & 0xFF);
+          s_hi[g] = e4m3_to_f32(b2 >> 8);
         } else {
-          s_lo[g] = s_hi[g] = e8m0_to_f32(sreg[cur][g]);
+          s_lo[g] = s_hi[g] = e8m0_to_f32(ss[n * 4 + lg]);
         }
       }
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         bf16x8 bt[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int row = wm * 64 + t * 16 + li;
-          bt[t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(stage + swz(row, lg * 4 + s)));
-        }
+        for (int t = 0; t < 4; ++t)
+          bt[t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(sa + swz_a(wm * 64 + t * 16 + li, lg * 4 + s)));
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const bf16x8 af = W_NV ? fp4x8_to_bf16(wreg[cur][g][s], s < 2 ? s_lo[g] : s_hi[g])
-                                 : fp4x8_to_bf16_pow2(wreg[cur][g][s], s_lo[g]);
+          const bf16x8 af = W_NV ? fp4x8_to_bf16(wq[g][s], s < 2 ? s_lo[g] : s_hi[g])
+                                 : fp4x8_to_bf16_pow2(wq[g][s], s_lo[g]);
 #pragma unroll
           for (int t = 0; t < 4; ++t) acc[g][t] = mfma16(af, bt[t], acc[g][t]);
         }
       }
-      if (kb + 1 < nk) tstore(lds + (cur ^ 1) * kPfStage);
+    };
+
+    uint8_t* st0 = lds;
+    uint8_t* st1 = lds + kPfStage;
+    PfRegs<A_NV> R0, R1;
+    __syncthreads();                                                 // previous tile done with LDS
+    fetch(R0, 0);
+    fetch(R1, 1);
+    store(R0, st0);
+    __syncthreads();
+    // Loads and stores are unconditional (past the last step they repeat it, from
+    // L2) so the compiler can count every wait exactly.
+    // Scheduling fences keep each fetch at the top of its half-iteration (the
+    // scheduler would otherwise sink the loads next to their use).
+    for (int kb = 0; kb < nk; kb += 2) {
+      fetch(R0, min(kb + 2, nk - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(st0);
+      __builtin_amdgcn_sched_barrier(0);
+      store(R1, st1);                                                // step kb + 1
+      __syncthreads();
+      fetch(R1, min(kb + 3, nk - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(st1);
+      __builtin_amdgcn_sched_barrier(0);
+      store(R0, st0);                                                // step kb + 2
       __syncthreads();
     }
 
@@ -263,7 +311,7 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_kernel(GemmArgs p) {
           const float g = acc[gp][t][i] * wglob[0];
           v[i] = NMAT == 2 ? silu_f(g) * (acc[gp + 2][t][i] * wglob[NMAT - 1]) : g;
         }
-        const int col = (NMAT == 2 ? nt * 128 + wn * 32 + gp * 16 : nt * 256 + wn * 64 + gp * 16) + 4 * lg;
+        const int col = nbase + (NMAT == 2 ? wn * 32 + gp * 16 : wn * 64 + gp * 16) + 4 * lg;
         const uint32_t b01 = pack_bf16x2(v[0], v[1]), b23 = pack_bf16x2(v[2], v[3]);
         if (p.out_bf16 && ok) *(u32x2*)(p.out_bf16 + ro * N + col) = u32x2{b01, b23};
         if (p.out_codes) {
@@ -306,7 +354,7 @@ moe_status launch_gemm_decode(const GemmArgs&, bool swiglu, bool w_nv, bool a_nv
 
 moe_status launch_gemm_prefill(const GemmArgs& a, bool swiglu, bool w_nv, bool a_nv, int64_t rows, hipStream_t stream) {
   const int bn = swiglu ? kPfBN / 2 : kPfBN;
-  if (a.N % bn != 0 || a.K % kPfBK != 0 || a.E > kPfMaxE) {
+  if (a.N % bn != 0 || a.K % (2 * kPfBK) != 0 || a.E > kPfMaxE) {
     // shapes the tiled kernel does not cover run on the weight-streaming kernel
     return launch_gemm_decode(a, swiglu, w_nv, a_nv, rows, stream);
   }
