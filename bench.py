@@ -30,10 +30,11 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP4_PEAK_TFLOPS = 10100.0      # MI355X dense fp4 MFMA
 MX_BYTES_PER_WEIGHT = 0.5 + 1.0 / 32.0
 
-# HBM bytes per launch of the gate/up GEMM measured with rocprofv3 --pmc
-# (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), keyed by
-# the hash of the kernel sources they were taken on; null once they change.
-MEASURED_TRAFFIC = {}
+# HBM bytes per launch of the decode gate/up GEMM at 64 tokens, measured with
+# rocprofv3 --pmc (FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000, the factors a plain
+# 1 GiB device copy gives), keyed by the hash of the kernel's sources at the
+# time; a changed kernel has no entry and reports null.
+MEASURED_TRAFFIC = {"083c4f21f3266982": 2181440463}
 
 
 def log(*a):
@@ -43,7 +44,7 @@ def log(*a):
 def kernel_source_hash():
     import hashlib
     h = hashlib.sha256()
-    for f in ("gemm_decode.hip", "gemm_prefill.hip", "gemm_common.h", "common.h"):
+    for f in ("gemm_decode.hip", "gemm_common.h", "common.h"):
         with open(os.path.join(ROOT, "block_scaled_fp4_group_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -136,7 +137,20 @@ def main():
     ap.add_argument("--rotate", type=int, default=4, help="independent decode weight sets")
     ap.add_argument("--no-extras", action="store_true", help="only the headline decode line")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB three times (the reference "
+                         "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for {args.gpus}).",
               file=sys.stderr, flush=True)
@@ -174,7 +188,7 @@ def main():
     gu_bytes = gate_up_bytes(main_r["D"], T, s)
     achieved = gu_bytes / (main_r["gate_up_ms"] / 1e3) / 1e9
     lb = layer_bytes(main_r["D"], T, s)
-    src_hash = kernel_source_hash()
+    src_hash = kernel_source_hash()   # of the decode kernel
     tr = MEASURED_TRAFFIC.get(src_hash)
     out = {
         "metric": "MoE-layer tokens/s at 1 MI355X (decode shape, HBM roofline)",
@@ -217,7 +231,7 @@ def main():
     out["extras"] = extras
     if not args.no_cpu:
         log("[bench] CPU oracle baseline")
-        sample = [0, 1, 2, 3]
+        sample = list(range(12))          # about 10 s of float64 work on the host
         v, dt, threads = cpu_baseline(s, Ws[0], main_r["x"], main_r["l"], None, sample)
         out["cpu_baseline"] = {"value": round(v, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
                                "sample": f"oracle.moe_layer on the decode T=64 batch: routing and permutation of all 64 "
