@@ -282,7 +282,7 @@ def prefill_lines(moe, synth, decode_lws, args):
         torch.cuda.synchronize()
         tc_ms.append(e0.elapsed_time(e1))
         assert int(cnt[2].item()) == 0
-        nvw[name] = moe.Weights(t.packed, sc, g)
+        nvw[name] = moe.Weights(t.packed, sc, g, scales_pow2=True)    # the transcode's scales are powers of two
     E = ww.shape.num_experts
     tc_bytes = 3 * E * 2048 * 4096 * (1 / 32 + 2 / 16)      # read E8M0, write 2x E4M3
     T = 4096

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libmoefp4.so")
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, 1, 2, 3, 4
 MOE_FP4_MX, MOE_FP4_NV = 0, 1
+MOE_FP4_SCALES_POW2 = 1
 MOE_ACT_BF16, MOE_ACT_NVFP4 = 0, 1
 MOE_EPI_NONE, MOE_EPI_SWIGLU = 0, 1
 MOE_ALGO_AUTO, MOE_ALGO_DECODE, MOE_ALGO_PREFILL = 0, 1, 2
@@ -35,7 +36,7 @@ class RouteParams(ctypes.Structure):
 class Fp4Weights(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int32), ("num_experts", ctypes.c_int32), ("n", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("packed", ctypes.c_void_p), ("scale", ctypes.c_void_p),
-                ("global_scale", ctypes.c_void_p)]
+                ("global_scale", ctypes.c_void_p), ("flags", ctypes.c_int32)]
 
 
 class Act(ctypes.Structure):
@@ -46,7 +47,7 @@ class Act(ctypes.Structure):
 
 class Out(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
-                ("output_scale", ctypes.c_float)]
+                ("output_scale", ctypes.c_float), ("dequant", ctypes.c_void_p)]
 
 
 def _load() -> ctypes.CDLL:
@@ -74,7 +75,7 @@ def _load() -> ctypes.CDLL:
     lib.fp4_transcode_mx_to_nv.restype = i32
     lib.fp4_transcode_mx_to_nv.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp, vp]
     lib.moe_quantize_nvfp4.restype = i32
-    lib.moe_quantize_nvfp4.argtypes = [vp, i64, i32, f32, vp, vp, vp]
+    lib.moe_quantize_nvfp4.argtypes = [vp, i64, i32, f32, vp, vp, vp, vp]
     return lib
 
 
@@ -148,6 +149,7 @@ class Weights:
     packed: torch.Tensor                  # u8 [E, n, k/2]
     scale: torch.Tensor                   # u8 [E, n, k/32] (MX) | [E, n, k/16] (NV)
     global_scale: Optional[torch.Tensor] = None   # f32 [E] (NV)
+    scales_pow2: bool = False             # NV: every scale byte is 0 or a power of two (a transcode)
 
     @property
     def format(self):
@@ -156,15 +158,17 @@ class Weights:
     def c(self) -> Fp4Weights:
         E, n, k2 = self.packed.shape
         return Fp4Weights(self.format, E, n, 2 * k2, self.packed.data_ptr(), self.scale.data_ptr(),
-                          None if self.global_scale is None else self.global_scale.data_ptr())
+                          None if self.global_scale is None else self.global_scale.data_ptr(),
+                          MOE_FP4_SCALES_POW2 if self.scales_pow2 else 0)
 
 
 def grouped_gemm(a: torch.Tensor, w0: Weights, w1: Optional[Weights], offsets: torch.Tensor, rows: int,
                  gather: Optional[torch.Tensor] = None, gather_div: int = 1, a_scales: Optional[torch.Tensor] = None,
                  input_scale: float = 1.0, out: Optional[torch.Tensor] = None, out_codes: Optional[torch.Tensor] = None,
                  out_scales: Optional[torch.Tensor] = None, output_scale: float = 1.0, want_bf16: bool = True,
-                 algo: int = MOE_ALGO_AUTO, stream=None):
-    """A: bf16 [rows_src, k] (W4A16) or NVFP4 codes u8 [rows_src, k/2] with ``a_scales`` (W4A4)."""
+                 out_dequant: Optional[torch.Tensor] = None, algo: int = MOE_ALGO_AUTO, stream=None):
+    """A: bf16 [rows_src, k] (W4A16) or NVFP4 codes u8 [rows_src, k/2] with ``a_scales`` (W4A4).
+    ``out_dequant``: bf16 [rows, n] receiving the NVFP4 output's values (codes x scale x output_scale)."""
     _dev(a, "a")
     n = w0.packed.shape[1]
     dev = a.device
@@ -174,7 +178,8 @@ def grouped_gemm(a: torch.Tensor, w0: Weights, w1: Optional[Weights], offsets: t
               None if a_scales is None else a_scales.data_ptr(), float(input_scale),
               None if gather is None else gather.data_ptr(), int(gather_div), a.shape[0])
     o = Out(None if out is None else out.data_ptr(), None if out_codes is None else out_codes.data_ptr(),
-            None if out_scales is None else out_scales.data_ptr(), float(output_scale))
+            None if out_scales is None else out_scales.data_ptr(), float(output_scale),
+            None if out_dequant is None else out_dequant.data_ptr())
     cw0 = w0.c()
     cw1 = w1.c() if w1 is not None else None
     epi = MOE_EPI_SWIGLU if w1 is not None else MOE_EPI_NONE
@@ -207,12 +212,14 @@ def transcode_mx_to_nv(mx_scale: torch.Tensor, packed: torch.Tensor, stream=None
     return nv, g, cnt
 
 
-def quantize_nvfp4(x: torch.Tensor, input_scale: float = 1.0, codes=None, scales=None, stream=None):
+def quantize_nvfp4(x: torch.Tensor, input_scale: float = 1.0, codes=None, scales=None, dequant=None, stream=None):
+    """-> (codes u8 [rows, k/2], scales u8 [rows, k/16]); ``dequant`` (bf16 [rows, k]) optionally
+    receives the NVFP4 values themselves."""
     rows, k = x.shape
     codes = torch.empty((rows, k // 2), dtype=torch.uint8, device=x.device) if codes is None else codes
     scales = torch.empty((rows, k // 16), dtype=torch.uint8, device=x.device) if scales is None else scales
-    _check(lib.moe_quantize_nvfp4(_ptr(x), rows, k, float(input_scale), _ptr(codes), _ptr(scales), _stream(stream)),
-           "moe_quantize_nvfp4")
+    _check(lib.moe_quantize_nvfp4(_ptr(x), rows, k, float(input_scale), _ptr(codes), _ptr(scales), _ptr(dequant),
+                                  _stream(stream)), "moe_quantize_nvfp4")
     return codes, scales
 
 

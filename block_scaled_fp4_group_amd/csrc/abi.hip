@@ -30,9 +30,9 @@ size_t permute_ws_bytes(int64_t R, int E);
 moe_status launch_permute(const int32_t*, int64_t, int, int, int32_t*, int32_t*, int32_t*, void*, hipStream_t);
 moe_status launch_combine(const void*, const int32_t*, const float*, const void*, int64_t, int, int, void*, hipStream_t);
 moe_status launch_transcode(const uint8_t*, const uint8_t*, int64_t, int, int, uint8_t*, float*, int64_t*, hipStream_t);
-moe_status launch_quant(const void*, int64_t, int, float, uint8_t*, uint8_t*, hipStream_t);
-moe_status launch_gemm_decode(const GemmArgs&, bool swiglu, bool w_nv, bool a_nv, int64_t rows, hipStream_t);
-moe_status launch_gemm_prefill(const GemmArgs&, bool swiglu, bool w_nv, bool a_nv, int64_t rows, hipStream_t);
+moe_status launch_quant(const void*, int64_t, int, float, uint8_t*, uint8_t*, void*, hipStream_t);
+moe_status launch_gemm_decode(const GemmArgs&, bool swiglu, int wf, bool a_nv, int64_t rows, hipStream_t);
+moe_status launch_gemm_prefill(const GemmArgs&, bool swiglu, int wf, bool a_nv, int64_t rows, hipStream_t);
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -120,6 +120,7 @@ static moe_status check_weights(const moe_fp4_weights* w, const char* name) {
   MOE_CHECK(w->packed && w->scale, "moe_fp4_grouped_gemm: %s NULL data", name);
   MOE_CHECK(aligned16(w->packed), "moe_fp4_grouped_gemm: %s codes not 16-byte aligned", name);
   if (w->format == MOE_FP4_NV) MOE_CHECK(w->global_scale != nullptr, "moe_fp4_grouped_gemm: %s NV without global", name);
+  MOE_CHECK((w->flags & ~MOE_FP4_SCALES_POW2) == 0, "moe_fp4_grouped_gemm: %s unknown flags 0x%x", name, w->flags);
   if (w->k % 128 != 0 || w->n % 16 != 0) {
     set_error("moe_fp4_grouped_gemm: %s needs k %% 128 == 0 and n %% 16 == 0 (n=%d k=%d)", name, w->n, w->k);
     return MOE_ERR_UNSUPPORTED;
@@ -138,7 +139,8 @@ moe_status moe_fp4_grouped_gemm(const moe_act* a, const moe_fp4_weights* w0, con
   if (epi == MOE_EPI_SWIGLU) {
     st = check_weights(w1, "w1");
     if (st) return st;
-    MOE_CHECK(w1->format == w0->format && w1->num_experts == w0->num_experts && w1->n == w0->n && w1->k == w0->k,
+    MOE_CHECK(w1->format == w0->format && w1->flags == w0->flags && w1->num_experts == w0->num_experts &&
+                  w1->n == w0->n && w1->k == w0->k,
               "moe_fp4_grouped_gemm: w0 / w1 differ");
   }
   MOE_CHECK(rows >= 0, "moe_fp4_grouped_gemm: rows < 0");
@@ -154,12 +156,12 @@ moe_status moe_fp4_grouped_gemm(const moe_act* a, const moe_fp4_weights* w0, con
     set_error("moe_fp4_grouped_gemm: activations larger than 2 GiB are not supported");
     return MOE_ERR_UNSUPPORTED;
   }
-  MOE_CHECK(out->data || out->codes, "moe_fp4_grouped_gemm: no output");
+  MOE_CHECK(out->data || out->codes || out->dequant, "moe_fp4_grouped_gemm: no output");
   if (out->data) MOE_CHECK(aligned16(out->data), "moe_fp4_grouped_gemm: output not 16-byte aligned");
-  if (out->codes) {
-    MOE_CHECK(out->scales != nullptr, "moe_fp4_grouped_gemm: NVFP4 output needs scales");
+  if (out->dequant) MOE_CHECK(aligned16(out->dequant), "moe_fp4_grouped_gemm: dequant output not 16-byte aligned");
+  if (out->codes) MOE_CHECK(out->scales != nullptr, "moe_fp4_grouped_gemm: NVFP4 output needs scales");
+  if (out->codes || out->dequant)
     MOE_CHECK(is_pow2_float(out->output_scale), "moe_fp4_grouped_gemm: output_scale must be a power of two");
-  }
   MOE_CHECK(algo >= MOE_ALGO_AUTO && algo <= MOE_ALGO_PREFILL, "moe_fp4_grouped_gemm: bad algo");
   if (rows == 0) return MOE_OK;
 
@@ -186,15 +188,19 @@ moe_status moe_fp4_grouped_gemm(const moe_act* a, const moe_fp4_weights* w0, con
   g.out_bf16 = (uint16_t*)out->data;
   g.out_codes = out->codes;
   g.out_scales = out->scales;
-  g.out_inv_g = out->codes ? 1.0f / out->output_scale : 1.0f;
+  const bool nvfp4_out = out->codes || out->dequant;
+  g.out_inv_g = nvfp4_out ? 1.0f / out->output_scale : 1.0f;
+  g.out_dq = (uint16_t*)out->dequant;
+  g.out_g = nvfp4_out ? out->output_scale : 1.0f;
 
   const bool swiglu = epi == MOE_EPI_SWIGLU;
-  const bool w_nv = w0->format == MOE_FP4_NV;
+  // weight scale format: 0 MXFP4, 1 NVFP4 with power-of-two scales, 2 NVFP4 with any scales
+  const int wf = w0->format == MOE_FP4_MX ? 0 : ((w0->flags & MOE_FP4_SCALES_POW2) ? 1 : 2);
   const bool a_nv = a->mode == MOE_ACT_NVFP4;
   int use = algo;
   if (use == MOE_ALGO_AUTO) use = (rows >= 32LL * g.E) ? MOE_ALGO_PREFILL : MOE_ALGO_DECODE;
-  if (use == MOE_ALGO_PREFILL) return launch_gemm_prefill(g, swiglu, w_nv, a_nv, rows, stream);
-  return launch_gemm_decode(g, swiglu, w_nv, a_nv, rows, stream);
+  if (use == MOE_ALGO_PREFILL) return launch_gemm_prefill(g, swiglu, wf, a_nv, rows, stream);
+  return launch_gemm_decode(g, swiglu, wf, a_nv, rows, stream);
 }
 
 moe_status moe_combine(const void* expert_out, const int32_t* slot_rows, const float* topk_weights,
@@ -225,14 +231,15 @@ moe_status fp4_transcode_mx_to_nv(const uint8_t* mx_scale, const uint8_t* packed
 }
 
 moe_status moe_quantize_nvfp4(const void* x, int64_t rows, int32_t k, float input_scale, uint8_t* codes,
-                              uint8_t* scales, hipStream_t stream) {
+                              uint8_t* scales, void* dequant, hipStream_t stream) {
   g_err[0] = 0;
   MOE_CHECK(rows >= 0 && k >= 32 && k % 32 == 0, "moe_quantize_nvfp4: needs k %% 32 == 0");
   MOE_CHECK(is_pow2_float(input_scale), "moe_quantize_nvfp4: input_scale must be a power of two");
   if (rows == 0) return MOE_OK;
   MOE_CHECK(x && codes && scales, "moe_quantize_nvfp4: NULL pointer");
   MOE_CHECK(aligned16(x) && ((uintptr_t)codes & 7u) == 0, "moe_quantize_nvfp4: misaligned buffers");
-  return launch_quant(x, rows, k, input_scale, codes, scales, stream);
+  if (dequant) MOE_CHECK(aligned16(dequant), "moe_quantize_nvfp4: dequant output not 16-byte aligned");
+  return launch_quant(x, rows, k, input_scale, codes, scales, dequant, stream);
 }
 
 }  // extern "C"

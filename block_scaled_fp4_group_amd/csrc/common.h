@@ -97,6 +97,17 @@ __device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t codes, float scale) {
   return fp4x8_to_bf16_general(codes, scale);
 }
 
+// 4 NVFP4 codes (16 bits, element 0 in the low nibble) times s * g -> 4 bf16
+// (two dwords).  code (2 significant bits) x E4M3 scale (4) x power of two is
+// exact in float and in bfloat16, so keeping the high half is exact.
+__device__ __forceinline__ u32x2 nvfp4_dequant4(uint32_t bits, float sg) {
+  const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(bits, 1.0f, 0);
+  const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(bits, 1.0f, 1);
+  const uint32_t w0 = (__float_as_uint(a[0] * sg) >> 16) | (__float_as_uint(a[1] * sg) & 0xFFFF0000u);
+  const uint32_t w1 = (__float_as_uint(b[0] * sg) >> 16) | (__float_as_uint(b[1] * sg) & 0xFFFF0000u);
+  return u32x2{w0, w1};
+}
+
 // ---------------------------------------------------------- buffer loads
 // Raw buffer descriptor over [base, base + bytes): loads whose offset falls
 // outside the range return zero and touch no memory (hardware range check).

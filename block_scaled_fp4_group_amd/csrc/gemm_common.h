@@ -24,6 +24,8 @@ struct GemmArgs {
   uint8_t* out_codes;             // [rows, N/2] or null
   uint8_t* out_scales;            // [rows, N/16]
   float out_inv_g;                // 1 / output global scale
+  uint16_t* out_dq;               // [rows, N] bf16 NVFP4 values (codes x scale x global) or null
+  float out_g;                    // output global scale
 };
 
 // Locate the j-th expert with at least one row (experts in index order).

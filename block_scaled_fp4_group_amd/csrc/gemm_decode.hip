@@ -60,8 +60,12 @@ __device__ __forceinline__ uint32_t quant4_across_lanes(const float* v, float in
   return bits;
 }
 
-template <int NMAT, bool W_NV>
+// WF: weight scale format -- 0 MXFP4 (E8M0 per 32), 1 NVFP4 whose E4M3 scales
+// are all powers of two (the exact MXFP4 transcode), 2 NVFP4 with any scales.
+template <int NMAT, int WF>
 struct DecodeWave {
+  static constexpr bool W_NV = WF != 0;
+  static constexpr bool W_GEN = WF == 2;     // general E4M3 scales: convert through float
   static constexpr int SWN = W_NV ? 2 : 1;   // dwordx4 per scale window
   rsrc_t wr_[NMAT];          // this expert's codes [N, K/2]
   rsrc_t sr_[NMAT];          // this expert's scales [N, K/32] | [N, K/16]
@@ -116,7 +120,8 @@ struct DecodeWave {
       }
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        bf16x8 wf = W_NV ? fp4x8_to_bf16(W.w[m][s], s < 2 ? s_lo : s_hi) : fp4x8_to_bf16_pow2(W.w[m][s], s_lo);
+        const float sc = s < 2 ? s_lo : s_hi;
+        const bf16x8 wf = W_GEN ? fp4x8_to_bf16_general(W.w[m][s], sc) : fp4x8_to_bf16_pow2(W.w[m][s], sc);
         acc[m] = mfma16(wf, af[s], acc[m]);
       }
     }
@@ -257,9 +262,11 @@ __device__ __forceinline__ void stage_rows(const GemmArgs& p, uint8_t* lds, int 
 __host__ __device__ constexpr int decode_rows_per_pass(int K) { return K > 2048 ? MOE_DEC_MR_4096 : MOE_DEC_MR_2048; }
 __host__ __device__ constexpr int decode_pitch(int K) { return K * 2 + 16; }
 
-template <int NMAT, int NWN, int KS, int NT, int NS, bool W_NV, bool A_NV>
+template <int NMAT, int NWN, int KS, int NT, int NS, int WF, bool A_NV>
 __global__ __launch_bounds__(NWN * KS * 64) void gemm_decode_kernel(GemmArgs p) {
-  constexpr int PF = NMAT == 2 ? MOE_DEC_PF2 : MOE_DEC_PF1, PA = 2;
+  constexpr bool W_NV = WF != 0;
+  // the general NVFP4 conversion needs more registers: a shorter weight ring
+  constexpr int PF = NMAT == 2 ? (WF == 2 ? 4 : MOE_DEC_PF2) : MOE_DEC_PF1, PA = 2;
   static_assert(KS == 1 || NT == 1, "the K split runs one tile per wave");
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int wn = wv % NWN, ks = wv / NWN;
@@ -275,7 +282,7 @@ __global__ __launch_bounds__(NWN * KS * 64) void gemm_decode_kernel(GemmArgs p) 
   const int ns = NS > 0 ? NS : (K / 128) / KS;                // own steps per tile (contiguous range)
   const int st0 = ks * ns;                                    // first global step
 
-  DecodeWave<NMAT, W_NV> dw;
+  DecodeWave<NMAT, WF> dw;
   dw.lg = lg;
   const uint32_t mat_codes = (uint32_t)N * (uint32_t)(K / 2);
   const uint32_t sc_row = (uint32_t)(W_NV ? K / 16 : K / 32);
@@ -331,20 +338,23 @@ __global__ __launch_bounds__(NWN * KS * 64) void gemm_decode_kernel(GemmArgs p) 
       const int64_t ro = rbase + li;
       const int col = nt0 + 4 * lg;
       if (p.out_bf16 && arow_ok) *(u32x2*)(p.out_bf16 + ro * N + col) = u32x2{b01, b23};
-      if (p.out_codes) {
+      if (p.out_codes || p.out_dq) {
         float q[4] = {bf16_lo(b01), bf16_hi(b01), bf16_lo(b23), bf16_hi(b23)};
         uint32_t sb;
         uint32_t bits = quant4_across_lanes(q, p.out_inv_g, sb);
         if (arow_ok) {
-          *(uint16_t*)(p.out_codes + ro * (N / 2) + col / 2) = (uint16_t)bits;
-          if (lg == 0) p.out_scales[ro * (N / 16) + nt0 / 16] = (uint8_t)sb;
+          if (p.out_codes) {
+            *(uint16_t*)(p.out_codes + ro * (N / 2) + col / 2) = (uint16_t)bits;
+            if (lg == 0) p.out_scales[ro * (N / 16) + nt0 / 16] = (uint8_t)sb;
+          }
+          if (p.out_dq) *(u32x2*)(p.out_dq + ro * N + col) = nvfp4_dequant4(bits, e4m3_to_f32(sb) * p.out_g);
         }
       }
     };
 
     if constexpr (NS > 0) {
       WStage<NMAT> wr[PF];
-      u32x4 sw0[NMAT][DecodeWave<NMAT, W_NV>::SWN];
+      u32x4 sw0[NMAT][DecodeWave<NMAT, WF>::SWN];
       dw.template prefetch<PF, NT, NS>(wr, sw0);          // weights in flight while the rows stage
       if (rbase != r0) __syncthreads();                  // previous pass done with the stage
       stage_rows<A_NV>(p, a_lds, rbase, mrows, pitch);
@@ -359,9 +369,9 @@ __global__ __launch_bounds__(NWN * KS * 64) void gemm_decode_kernel(GemmArgs p) 
   }
 }
 
-template <int NMAT, int NWN, int KS, int NT, int NS, bool W_NV, bool A_NV>
+template <int NMAT, int NWN, int KS, int NT, int NS, int WF, bool A_NV>
 static void launch_decode_one(const GemmArgs& a, int nact, hipStream_t stream) {
-  auto kern = gemm_decode_kernel<NMAT, NWN, KS, NT, NS, W_NV, A_NV>;
+  auto kern = gemm_decode_kernel<NMAT, NWN, KS, NT, NS, WF, A_NV>;
   const size_t lds = (size_t)decode_rows_per_pass(a.K) * decode_pitch(a.K);
   static bool attr_set = false;               // one-time opt-in to > 64 KB of LDS
   if (!attr_set) {
@@ -372,57 +382,58 @@ static void launch_decode_one(const GemmArgs& a, int nact, hipStream_t stream) {
 }
 
 template <int NMAT, int NWN, int KS, int NT, int NS>
-static void launch_decode_t(const GemmArgs& a, bool w_nv, bool a_nv, int nact, hipStream_t stream) {
-  if (w_nv) {
-    if (a_nv) launch_decode_one<NMAT, NWN, KS, NT, NS, true, true>(a, nact, stream);
-    else launch_decode_one<NMAT, NWN, KS, NT, NS, true, false>(a, nact, stream);
-  } else {
-    if (a_nv) launch_decode_one<NMAT, NWN, KS, NT, NS, false, true>(a, nact, stream);
-    else launch_decode_one<NMAT, NWN, KS, NT, NS, false, false>(a, nact, stream);
+static void launch_decode_t(const GemmArgs& a, int wf, bool a_nv, int nact, hipStream_t stream) {
+  switch (wf) {
+    case 0: a_nv ? launch_decode_one<NMAT, NWN, KS, NT, NS, 0, true>(a, nact, stream)
+                 : launch_decode_one<NMAT, NWN, KS, NT, NS, 0, false>(a, nact, stream); break;
+    case 1: a_nv ? launch_decode_one<NMAT, NWN, KS, NT, NS, 1, true>(a, nact, stream)
+                 : launch_decode_one<NMAT, NWN, KS, NT, NS, 1, false>(a, nact, stream); break;
+    default: a_nv ? launch_decode_one<NMAT, NWN, KS, NT, NS, 2, true>(a, nact, stream)
+                  : launch_decode_one<NMAT, NWN, KS, NT, NS, 2, false>(a, nact, stream); break;
   }
 }
 
 // K split into KS contiguous pieces of NS own steps (compile time for the model's K);
 // NT tiles of 16 rows per wave when K is not split.
 template <int NMAT, int NWN, int KS>
-static void launch_decode_k(const GemmArgs& a, bool w_nv, bool a_nv, int nact, hipStream_t stream) {
+static void launch_decode_k(const GemmArgs& a, int wf, bool a_nv, int nact, hipStream_t stream) {
   const int nsteps = a.K / 128;
   constexpr int NT = (KS > 1 || NMAT == 1) ? 1 : 2;
   if (KS == 1 && a.N % (16 * NWN * NT) == 0) {
-    if (nsteps == 32) return launch_decode_t<NMAT, NWN, KS, NT, 32>(a, w_nv, a_nv, nact, stream);
-    if (nsteps == 16) return launch_decode_t<NMAT, NWN, KS, NT, 16>(a, w_nv, a_nv, nact, stream);
+    if (nsteps == 32) return launch_decode_t<NMAT, NWN, KS, NT, 32>(a, wf, a_nv, nact, stream);
+    if (nsteps == 16) return launch_decode_t<NMAT, NWN, KS, NT, 16>(a, wf, a_nv, nact, stream);
   }
-  if (nsteps == 32) launch_decode_t<NMAT, NWN, KS, 1, 32 / KS>(a, w_nv, a_nv, nact, stream);
-  else if (nsteps == 16) launch_decode_t<NMAT, NWN, KS, 1, 16 / KS>(a, w_nv, a_nv, nact, stream);
-  else launch_decode_t<NMAT, NWN, KS, 1, 0>(a, w_nv, a_nv, nact, stream);
+  if (nsteps == 32) launch_decode_t<NMAT, NWN, KS, 1, 32 / KS>(a, wf, a_nv, nact, stream);
+  else if (nsteps == 16) launch_decode_t<NMAT, NWN, KS, 1, 16 / KS>(a, wf, a_nv, nact, stream);
+  else launch_decode_t<NMAT, NWN, KS, 1, 0>(a, wf, a_nv, nact, stream);
 }
 
 template <int NMAT>
-static void launch_decode_ks(const GemmArgs& a, bool w_nv, bool a_nv, int nact, hipStream_t stream) {
+static void launch_decode_ks(const GemmArgs& a, int wf, bool a_nv, int nact, hipStream_t stream) {
   // split K when too few waves would stream weights (aim for >= 8 waves per
   // CU); each piece keeps a multiple of 4 steps (one scale window per 4).
   const int64_t waves = (int64_t)nact * (a.N / 16);
   const int nsteps = a.K / 128;
   if (a.N % 64 != 0) {
-    launch_decode_k<NMAT, 1, 1>(a, w_nv, a_nv, nact, stream);
+    launch_decode_k<NMAT, 1, 1>(a, wf, a_nv, nact, stream);
   } else if (waves >= 2048 || nsteps % 8 != 0) {
-    launch_decode_k<NMAT, 4, 1>(a, w_nv, a_nv, nact, stream);
+    launch_decode_k<NMAT, 4, 1>(a, wf, a_nv, nact, stream);
   } else if (waves >= 1024 || nsteps % 16 != 0) {
-    launch_decode_k<NMAT, 2, 2>(a, w_nv, a_nv, nact, stream);
+    launch_decode_k<NMAT, 2, 2>(a, wf, a_nv, nact, stream);
   } else {
-    launch_decode_k<NMAT, 1, 4>(a, w_nv, a_nv, nact, stream);
+    launch_decode_k<NMAT, 1, 4>(a, wf, a_nv, nact, stream);
   }
 }
 
-moe_status launch_gemm_decode(const GemmArgs& a, bool swiglu, bool w_nv, bool a_nv, int64_t rows, hipStream_t stream) {
+moe_status launch_gemm_decode(const GemmArgs& a, bool swiglu, int wf, bool a_nv, int64_t rows, hipStream_t stream) {
   int nact = (int)std::min<int64_t>(a.E, rows);
   if (nact <= 0) return MOE_OK;
   if ((size_t)decode_rows_per_pass(a.K) * decode_pitch(a.K) > 96 * 1024) {
     set_error("moe_fp4_grouped_gemm: decode kernel supports k <= 4096 (k=%d)", a.K);
     return MOE_ERR_UNSUPPORTED;
   }
-  if (swiglu) launch_decode_ks<2>(a, w_nv, a_nv, nact, stream);
-  else launch_decode_ks<1>(a, w_nv, a_nv, nact, stream);
+  if (swiglu) launch_decode_ks<2>(a, wf, a_nv, nact, stream);
+  else launch_decode_ks<1>(a, wf, a_nv, nact, stream);
   return launch_status("moe_fp4_grouped_gemm(decode)");
 }
 

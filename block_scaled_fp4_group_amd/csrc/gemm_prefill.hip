@@ -154,9 +154,12 @@ __device__ __forceinline__ int pf_lrow(int wn, int g) {
   return NMAT == 2 ? (g >> 1) * 128 + wn * 32 + (g & 1) * 16 : wn * 64 + g * 16;
 }
 
-// One step from an LDS stage into acc[weight group][token group].
-template <int NMAT, bool W_NV>
+// One step from an LDS stage into acc[weight group][token group].  WF: weight
+// scale format -- 0 MXFP4, 1 NVFP4 with power-of-two scales (the exact MXFP4
+// transcode), 2 NVFP4 with any E4M3 scales (converted through float).
+template <int NMAT, int WF>
 __device__ __forceinline__ void pf_compute(const uint8_t* st, f32x4 (&acc)[4][4], int wm, int wn, int li, int lg) {
+  constexpr bool W_NV = WF != 0;
   const uint8_t* sa = st;
   const uint8_t* sw = st + kPfAStage;
   const uint8_t* ss = st + kPfAStage + kPfWStage;
@@ -186,8 +189,8 @@ __device__ __forceinline__ void pf_compute(const uint8_t* st, f32x4 (&acc)[4][4]
     if (s < 3) read_bt(bt[(s + 1) & 1], s + 1);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const bf16x8 af = W_NV ? fp4x8_to_bf16(wq[g][s], s < 2 ? s_lo[g] : s_hi[g])
-                             : fp4x8_to_bf16_pow2(wq[g][s], s_lo[g]);
+      const float sc = s < 2 ? s_lo[g] : s_hi[g];
+      const bf16x8 af = WF == 2 ? fp4x8_to_bf16_general(wq[g][s], sc) : fp4x8_to_bf16_pow2(wq[g][s], sc);
 #pragma unroll
       for (int t = 0; t < 4; ++t) acc[g][t] = mfma16(af, bt[s & 1][t], acc[g][t]);
     }
@@ -215,13 +218,16 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& p, const PfTile& T, 
       const int col = T.nbase + (NMAT == 2 ? wn * 32 + gp * 16 : wn * 64 + gp * 16) + 4 * lg;
       const uint32_t b01 = pack_bf16x2(v[0], v[1]), b23 = pack_bf16x2(v[2], v[3]);
       if (p.out_bf16 && ok) *(u32x2*)(p.out_bf16 + ro * N + col) = u32x2{b01, b23};
-      if (p.out_codes) {
+      if (p.out_codes || p.out_dq) {
         float q[4] = {bf16_lo(b01), bf16_hi(b01), bf16_lo(b23), bf16_hi(b23)};
         uint32_t sb;
         const uint32_t bits = quant4_lanes(q, p.out_inv_g, sb);
         if (ok) {
-          *(uint16_t*)(p.out_codes + ro * (N / 2) + col / 2) = (uint16_t)bits;
-          if (lg == 0) p.out_scales[ro * (N / 16) + (col - 4 * lg) / 16] = (uint8_t)sb;
+          if (p.out_codes) {
+            *(uint16_t*)(p.out_codes + ro * (N / 2) + col / 2) = (uint16_t)bits;
+            if (lg == 0) p.out_scales[ro * (N / 16) + (col - 4 * lg) / 16] = (uint8_t)sb;
+          }
+          if (p.out_dq) *(u32x2*)(p.out_dq + ro * N + col) = nvfp4_dequant4(bits, e4m3_to_f32(sb) * p.out_g);
         }
       }
     }
@@ -234,8 +240,9 @@ __device__ __forceinline__ uint8_t* pf_stage() {
   return S == 0 ? pf_stage0 : (S == 1 ? pf_stage1 : pf_stage2);
 }
 
-template <int NMAT, bool W_NV>
+template <int NMAT, int WF>
 __global__ __launch_bounds__(kPfThreads) void gemm_prefill_dma_kernel(GemmArgs p) {
+  constexpr bool W_NV = WF != 0;
   __shared__ int s_pref[kPfMaxE + 1];
   __shared__ int s_wc[kPfThreads / kWave];
   constexpr int kDmaPerStep = 7;                                     // direct-to-LDS loads per wave and step
@@ -243,7 +250,7 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_dma_kernel(GemmArgs p
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wv & 1, wn = wv >> 1;
+  const int wm = wv >> 2, wn = wv & 3;                               // SIMD s holds waves s (wm 0) and s + 4 (wm 1)
   const int li = lane & 15, lg = lane >> 4;
   const int K = p.K, N = p.N;
   const int ntn = N / (kPfBN / NMAT);
@@ -258,6 +265,9 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_dma_kernel(GemmArgs p
 
   for (int tile = t_begin; tile < t_end; tile += t_stride) {
     const PfTile T = locate_tile<NMAT>(p, s_pref, tile);
+    // a wave whose 64 token rows all lie past the tile's end skips its MFMA
+    // work (its SIMD then runs the other wave alone); it still loads and syncs
+    const bool active = wm * 64 < T.mrows;
     float wglob[NMAT];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) wglob[m] = W_NV ? p.w_global[m][T.e] : 1.0f;
@@ -318,7 +328,7 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_dma_kernel(GemmArgs p
       __builtin_amdgcn_sched_barrier(0);
       issue(std::integral_constant<int, (S + 2) % 3>(), min(k + 2, nk - 1));
       __builtin_amdgcn_sched_barrier(0);
-      pf_compute<NMAT, W_NV>(pf_stage<S>(), acc, wm, wn, li, lg);
+      if (active) pf_compute<NMAT, WF>(pf_stage<S>(), acc, wm, wn, li, lg);
     };
 
     __syncthreads();                                                 // previous tile done with the stages
@@ -346,15 +356,16 @@ struct PfRegs {
   uint32_t s;              // one dword of weight scales
 };
 
-template <int NMAT, bool W_NV>
+template <int NMAT, int WF>
 __global__ __launch_bounds__(kPfThreads) void gemm_prefill_nv_kernel(GemmArgs p) {
+  constexpr bool W_NV = WF != 0;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];      // 2 stages
   __shared__ int s_pref[kPfMaxE + 1];
   __shared__ int s_wc[kPfThreads / kWave];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  const int wm = wv & 1, wn = wv >> 1;
+  const int wm = wv >> 2, wn = wv & 3;                               // SIMD s holds waves s (wm 0) and s + 4 (wm 1)
   const int li = lane & 15, lg = lane >> 4;
   const int K = p.K, N = p.N;
   const int ntn = N / (kPfBN / NMAT);
@@ -375,6 +386,7 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_nv_kernel(GemmArgs p)
 
   for (int tile = t_begin; tile < t_end; tile += t_stride) {
     const PfTile T = locate_tile<NMAT>(p, s_pref, tile);
+    const bool active = wm * 64 < T.mrows;                           // as in the bf16 kernel
     rsrc_t wr[NMAT], sr[NMAT];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
@@ -450,13 +462,13 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_nv_kernel(GemmArgs p)
     for (int kb = 0; kb < nk; kb += 2) {
       fetch(R0, min(kb + 2, nk - 1));
       __builtin_amdgcn_sched_barrier(0);
-      pf_compute<NMAT, W_NV>(st0, acc, wm, wn, li, lg);
+      if (active) pf_compute<NMAT, WF>(st0, acc, wm, wn, li, lg);
       __builtin_amdgcn_sched_barrier(0);
       store(R1, st1);                                                // step kb + 1
       __syncthreads();
       fetch(R1, min(kb + 3, nk - 1));
       __builtin_amdgcn_sched_barrier(0);
-      pf_compute<NMAT, W_NV>(st1, acc, wm, wn, li, lg);
+      if (active) pf_compute<NMAT, WF>(st1, acc, wm, wn, li, lg);
       __builtin_amdgcn_sched_barrier(0);
       store(R0, st0);                                                // step kb + 2
       __syncthreads();
@@ -477,11 +489,11 @@ static int device_cus() {
   return cus;
 }
 
-template <int NMAT, bool W_NV, bool A_NV>
+template <int NMAT, int WF, bool A_NV>
 static void launch_prefill_one(const GemmArgs& a, hipStream_t stream) {
   // persistent: one workgroup per CU (8 waves); tiles are distributed on the device
   if (A_NV) {
-    auto kern = gemm_prefill_nv_kernel<NMAT, W_NV>;
+    auto kern = gemm_prefill_nv_kernel<NMAT, WF>;
     static bool attr_set = false;
     if (!attr_set) {
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kPfStage);
@@ -489,25 +501,29 @@ static void launch_prefill_one(const GemmArgs& a, hipStream_t stream) {
     }
     hipLaunchKernelGGL(kern, dim3(device_cus()), dim3(kPfThreads), 2 * kPfStage, stream, a);
   } else {
-    hipLaunchKernelGGL((gemm_prefill_dma_kernel<NMAT, W_NV>), dim3(device_cus()), dim3(kPfThreads), 0, stream, a);
+    hipLaunchKernelGGL((gemm_prefill_dma_kernel<NMAT, WF>), dim3(device_cus()), dim3(kPfThreads), 0, stream, a);
   }
 }
 
-moe_status launch_gemm_decode(const GemmArgs&, bool swiglu, bool w_nv, bool a_nv, int64_t rows, hipStream_t);
+template <int NMAT>
+static void launch_prefill_f(const GemmArgs& a, int wf, bool a_nv, hipStream_t stream) {
+  switch (wf) {
+    case 0: a_nv ? launch_prefill_one<NMAT, 0, true>(a, stream) : launch_prefill_one<NMAT, 0, false>(a, stream); break;
+    case 1: a_nv ? launch_prefill_one<NMAT, 1, true>(a, stream) : launch_prefill_one<NMAT, 1, false>(a, stream); break;
+    default: a_nv ? launch_prefill_one<NMAT, 2, true>(a, stream) : launch_prefill_one<NMAT, 2, false>(a, stream); break;
+  }
+}
 
-moe_status launch_gemm_prefill(const GemmArgs& a, bool swiglu, bool w_nv, bool a_nv, int64_t rows, hipStream_t stream) {
+moe_status launch_gemm_decode(const GemmArgs&, bool swiglu, int wf, bool a_nv, int64_t rows, hipStream_t);
+
+moe_status launch_gemm_prefill(const GemmArgs& a, bool swiglu, int wf, bool a_nv, int64_t rows, hipStream_t stream) {
   const int bn = swiglu ? kPfBN / 2 : kPfBN;
   if (a.N % bn != 0 || a.K % (2 * kPfBK) != 0 || a.E > kPfMaxE) {
     // shapes the tiled kernels do not cover run on the weight-streaming kernel
-    return launch_gemm_decode(a, swiglu, w_nv, a_nv, rows, stream);
+    return launch_gemm_decode(a, swiglu, wf, a_nv, rows, stream);
   }
-  if (swiglu) {
-    if (w_nv) a_nv ? launch_prefill_one<2, true, true>(a, stream) : launch_prefill_one<2, true, false>(a, stream);
-    else a_nv ? launch_prefill_one<2, false, true>(a, stream) : launch_prefill_one<2, false, false>(a, stream);
-  } else {
-    if (w_nv) a_nv ? launch_prefill_one<1, true, true>(a, stream) : launch_prefill_one<1, true, false>(a, stream);
-    else a_nv ? launch_prefill_one<1, false, true>(a, stream) : launch_prefill_one<1, false, false>(a, stream);
-  }
+  if (swiglu) launch_prefill_f<2>(a, wf, a_nv, stream);
+  else launch_prefill_f<1>(a, wf, a_nv, stream);
   return launch_status("moe_fp4_grouped_gemm(prefill)");
 }
 

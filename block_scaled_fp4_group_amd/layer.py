@@ -4,6 +4,13 @@ route -> permute -> [W4A4: quantise x] -> gate/up grouped GEMM with SwiGLU
 (writes z, bf16 or NVFP4) -> down grouped GEMM -> weighted combine.  Buffers
 are allocated once for a maximum token count, so a forward pass allocates
 nothing and can be captured in a HIP graph.
+
+W4A4: x is quantised to NVFP4 and the gate/up epilogue quantises z to NVFP4;
+both GEMMs then multiply the NVFP4 values themselves, handed over as exact
+bfloat16 (code x scale x global has at most 6 significant bits), so they run
+the bf16-input kernels on exactly the W4A4 operands.  ``a_mode="nvfp4_codes"``
+feeds the GEMMs the NVFP4 codes and scales instead (the same products, with
+the dequantisation inside the GEMM).
 """
 from __future__ import annotations
 
@@ -26,11 +33,12 @@ class LayerWeights:
 class MoELayer:
     def __init__(self, weights: LayerWeights, num_experts: int, n_group: int, topk_group: int, top_k: int,
                  routed_scaling_factor: float, max_tokens: int, act_mode: str = "bf16", input_scale: float = 1.0,
-                 keep_z_bf16: bool = False, device="cuda"):
+                 keep_z_bf16: bool = False, a_mode: str = "dequant", device="cuda"):
         self.w = weights
         self.E, self.n_group, self.topk_group, self.top_k = num_experts, n_group, topk_group, top_k
         self.scale = routed_scaling_factor
         self.act_mode = act_mode
+        self.a_mode = a_mode
         self.input_scale = input_scale
         E, I, H2 = weights.gate.packed.shape
         H = 2 * H2
@@ -53,6 +61,9 @@ class MoELayer:
             self.x_scales = torch.empty((T, H // 16), dtype=torch.uint8, device=dev)
             self.z_codes = torch.empty((R, I // 2), dtype=torch.uint8, device=dev)
             self.z_scales = torch.empty((R, I // 16), dtype=torch.uint8, device=dev)
+            if a_mode == "dequant":
+                self.x_dq = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+                self.z_dq = torch.empty((R, I), dtype=torch.bfloat16, device=dev)
 
     def forward(self, x: torch.Tensor, logits: torch.Tensor, bias: Optional[torch.Tensor] = None,
                 residual: Optional[torch.Tensor] = None, algo: int = MOE_ALGO_AUTO, y: Optional[torch.Tensor] = None,
@@ -70,7 +81,20 @@ class MoELayer:
         permute(ids, self.E, self.ws, self.offsets, self.sorted_slots[:R], self.slot_rows[:R])
         z = None if self.z is None else self.z[:R]
         o = self.o[:R]
-        if self.act_mode == "nvfp4":
+        if self.act_mode == "nvfp4" and self.a_mode == "dequant":
+            xdq = self.x_dq[:T]
+            quantize_nvfp4(x, self.input_scale, self.x_codes[:T], self.x_scales[:T], dequant=xdq)
+            keep = z is not None
+            mark("gate_up", 0)
+            grouped_gemm(xdq, self.w.gate, self.w.up, self.offsets, R, gather=self.sorted_slots[:R],
+                         gather_div=self.top_k, out=z, out_codes=self.z_codes[:R] if keep else None,
+                         out_scales=self.z_scales[:R] if keep else None, output_scale=self.input_scale,
+                         want_bf16=keep, out_dequant=self.z_dq[:R], algo=algo)
+            mark("gate_up", 1)
+            mark("down", 0)
+            grouped_gemm(self.z_dq[:R], self.w.down, None, self.offsets, R, out=o, algo=algo)
+            mark("down", 1)
+        elif self.act_mode == "nvfp4":
             xc, xs = quantize_nvfp4(x, self.input_scale, self.x_codes[:T], self.x_scales[:T])
             mark("gate_up", 0)
             grouped_gemm(xc, self.w.gate, self.w.up, self.offsets, R, gather=self.sorted_slots[:R],

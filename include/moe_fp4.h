@@ -112,6 +112,13 @@ moe_status moe_permute(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_
  */
 typedef enum { MOE_FP4_MX = 0, MOE_FP4_NV = 1 } moe_fp4_format;
 
+/* moe_fp4_weights.flags */
+#define MOE_FP4_SCALES_POW2 1 /* NV: every E4M3 scale byte is zero or a power of two (true of
+                                 fp4_transcode_mx_to_nv output); codes then convert with the
+                                 scale applied by the convert instruction itself.  Setting it
+                                 for other scales gives wrong results; leaving it clear is
+                                 always correct (conversion through float). */
+
 typedef struct {
   moe_fp4_format format;
   int32_t num_experts;
@@ -120,6 +127,7 @@ typedef struct {
   const uint8_t* packed;      /* codes [E, n, k/2] ("weight_packed")                    */
   const uint8_t* scale;       /* MX: E8M0 [E, n, k/32] | NV: E4M3 [E, n, k/16]          */
   const float* global_scale;  /* NV: float [E] (per expert matrix) | MX: NULL            */
+  int32_t flags;              /* MOE_FP4_SCALES_POW2 or 0 (ignored for MX)              */
 } moe_fp4_weights;
 
 typedef enum { MOE_ACT_BF16 = 0 /* W4A16 */, MOE_ACT_NVFP4 = 1 /* W4A4 */ } moe_act_mode;
@@ -141,6 +149,10 @@ typedef struct {
   uint8_t* codes;             /* NVFP4 codes [rows, n/2] or NULL (needs n % 16 == 0)       */
   uint8_t* scales;            /* E4M3 [rows, n/16] (with codes)                           */
   float output_scale;         /* global scale of the NVFP4 output (a power of two)        */
+  void* dequant;              /* bf16 [rows, n] or NULL: the NVFP4 values themselves,
+                                 codes x scale x output_scale (exact in bfloat16), so a
+                                 following bf16-input GEMM computes on exactly the NVFP4
+                                 operand (W4A4 down projection)                         */
 } moe_out;
 
 #define MOE_ALGO_AUTO 0       /* choose by rows per expert                                */
@@ -183,9 +195,11 @@ moe_status fp4_transcode_mx_to_nv(const uint8_t* mx_scale, const uint8_t* packed
  * (+0 codes when s == 0).  g = input_scale must be a power of two.
  * (MOPD-NVFP4 card, "About NVFP4 quantization" and "Quantization Details".)
  *   x bf16 [rows, k]; codes u8 [rows, k/2]; scales u8 [rows, k/16]; k % 32 == 0.
+ *   dequant: bf16 [rows, k] or NULL; receives the NVFP4 values codes x s x g
+ *   (exact in bfloat16), the operand a bf16-input GEMM multiplies for W4A4.
  */
 moe_status moe_quantize_nvfp4(const void* x, int64_t rows, int32_t k, float input_scale,
-                              uint8_t* codes, uint8_t* scales, hipStream_t stream);
+                              uint8_t* codes, uint8_t* scales, void* dequant, hipStream_t stream);
 
 #ifdef __cplusplus
 }

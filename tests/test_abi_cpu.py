@@ -92,9 +92,9 @@ def test_combine_transcode_quant_reject():
     _err(moe.lib.fp4_transcode_mx_to_nv(FAKE, FAKE, 2, 16, 48, FAKE, FAKE, cnt, None), moe.MOE_ERR_INVALID)
     _err(moe.lib.fp4_transcode_mx_to_nv(FAKE, FAKE, 2, 8, 64, FAKE, FAKE, cnt, None), moe.MOE_ERR_INVALID)
     _err(moe.lib.fp4_transcode_mx_to_nv(FAKE, FAKE, 2, 16, 64, FAKE, FAKE, None, None), moe.MOE_ERR_INVALID)
-    _err(moe.lib.moe_quantize_nvfp4(FAKE, 4, 48, 1.0, FAKE, FAKE, None), moe.MOE_ERR_INVALID)
-    _err(moe.lib.moe_quantize_nvfp4(FAKE, 4, 64, 0.3, FAKE, FAKE, None), moe.MOE_ERR_INVALID)
-    assert moe.lib.moe_quantize_nvfp4(None, 0, 64, 1.0, None, None, None) == moe.MOE_OK
+    _err(moe.lib.moe_quantize_nvfp4(FAKE, 4, 48, 1.0, FAKE, FAKE, None, None), moe.MOE_ERR_INVALID)
+    _err(moe.lib.moe_quantize_nvfp4(FAKE, 4, 64, 0.3, FAKE, FAKE, None, None), moe.MOE_ERR_INVALID)
+    assert moe.lib.moe_quantize_nvfp4(None, 0, 64, 1.0, None, None, None, None) == moe.MOE_OK
 
 
 def test_status_strings():

@@ -141,10 +141,13 @@ def test_quantize_nvfp4_parity(g):
         x[3 + j, 40] = -amax
     xb = synth.bf16_bits_from_f32(x)
     c_ref, s_ref = oracle.quantize_nvfp4(xb, g)
-    c, s = moe.quantize_nvfp4(dev_bf16(xb), g)
+    dq = torch.empty((rows, k), dtype=torch.bfloat16, device="cuda")
+    c, s = moe.quantize_nvfp4(dev_bf16(xb), g, dequant=dq)
     torch.cuda.synchronize()
     assert np.array_equal(host(s), s_ref)
     assert np.array_equal(host(c), c_ref)
+    # the dequantised output holds exactly the NVFP4 values codes x scale x g
+    assert np.array_equal(bf16_to_f64(host_bf16_bits(dq)), oracle.dequant_nvfp4_act(c_ref, s_ref, g))
 
 
 def test_quantize_nvfp4_outlier_rows():
@@ -226,7 +229,9 @@ def test_combine_parity(with_resid):
 
 
 # ------------------------------------------------------------ grouped GEMM
-def _gemm_problem(seed, E, n, k, counts, nsrc, fmt, general_nv=False):
+def _gemm_problem(seed, E, n, k, counts, nsrc, fmt, general_nv=False, pow2_flag=True):
+    """fmt "mx" or "nv"; NV scales are the exact transcode (powers of two; declared
+    as such when pow2_flag) or, with general_nv, arbitrary E4M3 bytes."""
     rng = np.random.default_rng(seed)
     packed, mx = synth.random_mx_small(seed, E, n, k)
     if fmt == "mx":
@@ -241,7 +246,7 @@ def _gemm_problem(seed, E, n, k, counts, nsrc, fmt, general_nv=False):
             sc, g, _ = oracle.transcode_mx_to_nv(mx, packed)
         wt = (packed, sc, g)
         dq = [oracle.dequant_nv(packed[e], sc[e], g[e]) for e in range(E)]
-        wdev = moe.Weights(dev_u8(packed), dev_u8(sc), dev_f32(g))
+        wdev = moe.Weights(dev_u8(packed), dev_u8(sc), dev_f32(g), scales_pow2=(not general_nv) and pow2_flag)
     return wdev, dq
 
 
@@ -249,20 +254,21 @@ GEMM_COUNTS = [0, 1, 17, 300, 1000, 33, 0, 64]
 
 
 @pytest.mark.parametrize("algo", [moe.MOE_ALGO_DECODE, moe.MOE_ALGO_PREFILL])
-@pytest.mark.parametrize("fmt,general", [("mx", False), ("nv", False), ("nv", True)])
+@pytest.mark.parametrize("fmt,general,flag", [("mx", False, True), ("nv", False, True), ("nv", False, False),
+                                               ("nv", True, False)])
 @pytest.mark.parametrize("amode", ["bf16", "nvfp4"])
-def test_grouped_gemm_swiglu_parity(algo, fmt, general, amode):
+def test_grouped_gemm_swiglu_parity(algo, fmt, general, flag, amode):
     E, H, I = 8, 512, 256
     counts = np.array(GEMM_COUNTS)
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     R = int(offsets[-1])
     tsrc = 700
-    say(f"gemm swiglu algo={algo} fmt={fmt} general={general} amode={amode} R={R}")
+    say(f"gemm swiglu algo={algo} fmt={fmt} general={general} pow2 flag={flag} amode={amode} R={R}")
     x = synth.random_bf16(41, (tsrc, H))
     rng = np.random.default_rng(42)
     gather = rng.integers(0, tsrc * 8, size=R).astype(np.int32)          # slot ids; row = slot // 8
-    wg, dg = _gemm_problem(43, E, I, H, counts, tsrc, fmt, general)
-    wu, du = _gemm_problem(44, E, I, H, counts, tsrc, fmt, general)
+    wg, dg = _gemm_problem(43, E, I, H, counts, tsrc, fmt, general, flag)
+    wu, du = _gemm_problem(44, E, I, H, counts, tsrc, fmt, general, flag)
     if amode == "nvfp4":
         xc, xs = oracle.quantize_nvfp4(x, 1.0)
         a_val = oracle.dequant_nvfp4_act(xc, xs)
@@ -272,8 +278,9 @@ def test_grouped_gemm_swiglu_parity(algo, fmt, general, amode):
         a_dev, a_sc = dev_bf16(x), None
     zc = torch.empty((R, I // 2), dtype=torch.uint8, device="cuda")
     zs = torch.empty((R, I // 16), dtype=torch.uint8, device="cuda")
+    zdq = torch.empty((R, I), dtype=torch.bfloat16, device="cuda")
     z = moe.grouped_gemm(a_dev, wg, wu, dev_i32(offsets), R, gather=dev_i32(gather), gather_div=8, a_scales=a_sc,
-                         out_codes=zc, out_scales=zs, algo=algo)
+                         out_codes=zc, out_scales=zs, out_dequant=zdq, algo=algo)
     z2 = moe.grouped_gemm(a_dev, wg, wu, dev_i32(offsets), R, gather=dev_i32(gather), gather_div=8, a_scales=a_sc,
                           algo=algo)
     torch.cuda.synchronize()
@@ -291,6 +298,8 @@ def test_grouped_gemm_swiglu_parity(algo, fmt, general, amode):
     c_ref, s_ref = oracle.quantize_nvfp4(zb, 1.0)
     assert np.array_equal(host(zs), s_ref)
     assert np.array_equal(host(zc), c_ref)
+    # and the dequantised NVFP4 output holds exactly those values
+    assert np.array_equal(bf16_to_f64(host_bf16_bits(zdq)), oracle.dequant_nvfp4_act(c_ref, s_ref))
 
 
 @pytest.mark.parametrize("algo", [moe.MOE_ALGO_DECODE, moe.MOE_ALGO_PREFILL])

@@ -41,7 +41,7 @@ def upload_weights(W, fmt):
         t = W[name]
         if fmt == "mx":
             return moe.Weights(dev_u8(t[0]), dev_u8(t[1]))
-        return moe.Weights(dev_u8(t[0]), dev_u8(t[1]), dev_f32(t[2]))
+        return moe.Weights(dev_u8(t[0]), dev_u8(t[1]), dev_f32(t[2]), scales_pow2=True)   # transcoded MX
     return moe.LayerWeights(one("gate"), one("up"), one("down"))
 
 
@@ -147,7 +147,7 @@ def test_decode_mx_equals_nv_bitwise(decode_weights):
         t = getattr(dw, name)
         E, n, kb = t.scale.shape
         sc, g, cnt = moe.transcode_mx_to_nv(t.scale, t.packed)
-        nvw[name] = moe.Weights(t.packed, sc, g)
+        nvw[name] = moe.Weights(t.packed, sc, g, scales_pow2=True)
         torch.cuda.synchronize()
         assert host(cnt)[2] == 0
     dnv = moe.LayerWeights(nvw["gate"], nvw["up"], nvw["down"])
@@ -185,6 +185,31 @@ def test_w4a4_layer():
     check_layer(w, 4096, nv, "nv", "nvfp4", [1, 2048, 4095])
 
 
+def test_w4a4_routes_agree():
+    """The W4A4 layer fed NVFP4 codes + scales to the GEMMs and fed their exact
+    bf16 values give the same bytes (same products, same accumulation order)."""
+    w = synth.WORKLOADS["w4a4"]
+    s = w.shape
+    W = synth.expert_weights(w)
+    nvw = {}
+    for name in ("gate", "up", "down"):
+        packed = dev_u8(W[name][0])
+        sc, g, _ = moe.transcode_mx_to_nv(dev_u8(W[name][1]), packed)      # byte-exact (transcode tests)
+        nvw[name] = moe.Weights(packed, sc, g, scales_pow2=True)
+    dw = moe.LayerWeights(nvw["gate"], nvw["up"], nvw["down"])
+    for T, algo in ((64, moe.MOE_ALGO_DECODE), (2048, moe.MOE_ALGO_PREFILL)):
+        say(f"w4a4 routes T={T} algo={algo}")
+        x = dev_bf16(synth.activations(w, T))
+        l = dev_f32(synth.logits(w, T))
+        outs = []
+        for a_mode in ("dequant", "nvfp4_codes"):
+            layer = moe.MoELayer(dw, s.num_experts, s.n_group, s.topk_group, s.top_k, s.routed_scaling_factor, T,
+                                 act_mode="nvfp4", a_mode=a_mode)
+            outs.append(host_bf16_bits(layer.forward(x, l, algo=algo)).copy())
+        torch.cuda.synchronize()
+        assert np.array_equal(outs[0], outs[1])
+
+
 @pytest.mark.parametrize("amax", synth.OUTLIER_AMAX)
 def test_w4a4_down_outliers(amax):
     """Down projection alone on N(0,1) inputs with 0.1% outliers (saturation at 2688)."""
@@ -198,7 +223,7 @@ def test_w4a4_down_outliers(amax):
     Wd = synth.mx_matrix(2, 0, synth.T_DOWN_CODES, synth.T_DOWN_EXP, E, s.hidden, s.inter)
     sc, g, _ = oracle.transcode_mx_to_nv(Wd[1], Wd[0])
     zc, zs = moe.quantize_nvfp4(dev_bf16(z), 1.0)
-    wdev = moe.Weights(dev_u8(Wd[0]), dev_u8(sc), dev_f32(g))
+    wdev = moe.Weights(dev_u8(Wd[0]), dev_u8(sc), dev_f32(g), scales_pow2=True)
     o = moe.grouped_gemm(zc, wdev, None, dev_i32_like(offsets), rows, a_scales=zs)
     torch.cuda.synchronize()
     c_ref, s_ref = oracle.quantize_nvfp4(z, 1.0)
