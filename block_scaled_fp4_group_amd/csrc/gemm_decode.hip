@@ -6,8 +6,9 @@
 // exact NVFP4 transcode; accumulation is FP32 ("AxionML / MiMo-V2.6-Flash-
 // MOPD-NVFP4", "About NVFP4 quantization").
 //
-// Work split: blockIdx.y picks the j-th expert that has rows, blockIdx.x a tile
-// of 16*NWN weight rows (output features).  Each wave owns 16 weight rows and
+// Work split: a workgroup takes the j-th expert that has rows and a tile of
+// 16*NWN*NT weight rows (output features), laid out so that one expert's
+// workgroups run on one XCD.  Each wave owns 16 weight rows and
 // walks its K range in steps of 128: in one step, lane group g (lanes
 // 16g..16g+15) reads one whole 32-value block (16 code bytes) of each of the 16
 // rows, dequantises it in registers (E2M1 x power-of-two scale -> bf16 with the
@@ -273,12 +274,18 @@ __global__ __launch_bounds__(NWN * KS * 64) void gemm_decode_kernel(GemmArgs p) 
   const int li = lane & 15, lg = lane >> 4;
   extern __shared__ __attribute__((aligned(16))) uint8_t a_lds[];
 
-  int e, r0, r1;
-  if (!find_active_expert(p.offsets, p.E, p.rows, blockIdx.y, e, r0, r1)) return;
+  // 1-D grid, XCD-aware: workgroup b runs on XCD b % 8; the n-blocks of the
+  // j-th active expert all get the same b % 8 (= j % 8), so they share that
+  // XCD's L2 for the expert's token rows
   const int K = p.K, N = p.N;
+  const int nxb = N / (16 * NWN * NT);                        // n-blocks per expert
+  const int xcd = blockIdx.x & 7, rank = blockIdx.x >> 3;
+  const int xb = rank % nxb, jexp = (rank / nxb) * 8 + xcd;
+  int e, r0, r1;
+  if (!find_active_expert(p.offsets, p.E, p.rows, jexp, e, r0, r1)) return;
   const int MR = decode_rows_per_pass(K), pitch = decode_pitch(K);
   // this wave's NT tiles of 16 weight rows: n0 + 16 * NWN * t
-  const int n0 = blockIdx.x * (16 * NWN * NT) + wn * 16;
+  const int n0 = xb * (16 * NWN * NT) + wn * 16;
   const int ns = NS > 0 ? NS : (K / 128) / KS;                // own steps per tile (contiguous range)
   const int st0 = ks * ns;                                    // first global step
 
@@ -378,7 +385,9 @@ static void launch_decode_one(const GemmArgs& a, int nact, hipStream_t stream) {
     hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3(a.N / (16 * NWN * NT), nact), dim3(NWN * KS * 64), lds, stream, a);
+  const int nxb = a.N / (16 * NWN * NT);
+  const int64_t blocks = (int64_t)nxb * ((nact + 7) / 8) * 8;   // whole groups of 8 experts (see the kernel)
+  hipLaunchKernelGGL(kern, dim3((uint32_t)blocks), dim3(NWN * KS * 64), lds, stream, a);
 }
 
 template <int NMAT, int NWN, int KS, int NT, int NS>

@@ -64,21 +64,23 @@ __device__ __forceinline__ void rank_subchunks(const int32_t* __restrict__ ids, 
 
 // cnt[sub][e - e0] <- group sizes of the sub-chunks, then exclusive prefix over
 // the sub-chunks.  Returns (in tot, for threads e-e0 < 256) the chunk total.
+// Only the first nsub sub-chunks hold slots (a short last chunk uses fewer).
 __device__ __forceinline__ void subchunk_prefix(const SubRanks& r, int e0, uint16_t (*cnt)[kERange],
-                                                int32_t* tot) {
+                                                int32_t* tot, int nsub) {
   const int w = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < kPermSub * kERange; i += kPermThreads) (&cnt[0][0])[i] = 0;
+  for (int i = threadIdx.x; i < nsub * kERange; i += kPermThreads) (&cnt[0][0])[i] = 0;
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < kSubPerWave; ++q) {
     int e = r.e[q];
     if (e >= e0 && e < e0 + kERange && r.rank[q] == 0) cnt[w * kSubPerWave + q][e - e0] = (uint16_t)r.size[q];
+    // (a sub-chunk past nsub holds no slot, so e < 0 there and nothing is written)
   }
   __syncthreads();
   {
     int j = threadIdx.x;    // one expert of the range per thread
     int32_t run = 0;
-    for (int sub = 0; sub < kPermSub; ++sub) {
+    for (int sub = 0; sub < nsub; ++sub) {
       int32_t c = cnt[sub][j];
       cnt[sub][j] = (uint16_t)run;
       run += c;
@@ -138,9 +140,10 @@ __global__ __launch_bounds__(kPermThreads) void permute_single(const int32_t* __
   __shared__ int32_t range_total;
   SubRanks r;
   rank_subchunks(ids, R, E, nbits, 0, r);
+  const int nsub = (int)min((int64_t)kPermSub, (R + kWave - 1) / kWave);
   int32_t carry = 0;
   for (int e0 = 0; e0 < E; e0 += kERange) {
-    subchunk_prefix(r, e0, cnt, tot);
+    subchunk_prefix(r, e0, cnt, tot, nsub);
     int j = threadIdx.x;
     int32_t v = (e0 + j < E) ? tot[j] : 0;
     int32_t ex = block_excl_scan(v, wsum, &range_total);
@@ -218,8 +221,9 @@ __global__ __launch_bounds__(kPermThreads) void permute_scatter(const int32_t* _
   SubRanks r;
   rank_subchunks(ids, R, E, nbits, base, r);
   const int32_t* brow = table + (int64_t)blockIdx.x * E;
+  const int nsub = (int)min((int64_t)kPermSub, (R - base + kWave - 1) / kWave);
   for (int e0 = 0; e0 < E; e0 += kERange) {
-    subchunk_prefix(r, e0, cnt, tot);
+    subchunk_prefix(r, e0, cnt, tot, nsub);
     write_rows(r, e0, cnt, brow + e0, R, base, sorted_slots, slot_rows);
     __syncthreads();
   }
