@@ -275,9 +275,14 @@ def prefill_lines(moe, synth, decode_lws, args):
     tc_ms = []
     for name in ("gate", "up", "down"):
         t = getattr(src, name)
+        M, n, kb = t.scale.shape
+        sc = torch.empty((M, n, kb * 2), dtype=torch.uint8, device="cuda")
+        g = torch.empty(M, dtype=torch.float32, device="cuda")
+        cnt = torch.empty(4, dtype=torch.int64, device="cuda")
+        moe.transcode_mx_to_nv(t.scale, t.packed, sc, g, cnt)          # warm-up (outputs preallocated)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        sc, g, cnt = moe.transcode_mx_to_nv(t.scale, t.packed)
+        moe.transcode_mx_to_nv(t.scale, t.packed, sc, g, cnt)
         e1.record()
         torch.cuda.synchronize()
         tc_ms.append(e0.elapsed_time(e1))

@@ -199,14 +199,15 @@ def combine(expert_out: torch.Tensor, slot_rows: torch.Tensor, topk_weights: tor
     return y
 
 
-def transcode_mx_to_nv(mx_scale: torch.Tensor, packed: torch.Tensor, stream=None):
-    """mx_scale u8 [M, n, k/32], packed u8 [M, n, k/2] -> (nv_scale, global f32 [M], counters i64 [4])."""
+def transcode_mx_to_nv(mx_scale: torch.Tensor, packed: torch.Tensor, nv=None, g=None, cnt=None, stream=None):
+    """mx_scale u8 [M, n, k/32], packed u8 [M, n, k/2] -> (nv_scale, global f32 [M], counters i64 [4])
+    (written into ``nv``, ``g``, ``cnt`` when given)."""
     M, n, kb = mx_scale.shape
     k = kb * 32
     dev = mx_scale.device
-    nv = torch.empty((M, n, k // 16), dtype=torch.uint8, device=dev)
-    g = torch.empty(M, dtype=torch.float32, device=dev)
-    cnt = torch.empty(4, dtype=torch.int64, device=dev)
+    nv = torch.empty((M, n, k // 16), dtype=torch.uint8, device=dev) if nv is None else nv
+    g = torch.empty(M, dtype=torch.float32, device=dev) if g is None else g
+    cnt = torch.empty(4, dtype=torch.int64, device=dev) if cnt is None else cnt
     _check(lib.fp4_transcode_mx_to_nv(_ptr(mx_scale), _ptr(packed), M, n, k, _ptr(nv), _ptr(g), _ptr(cnt),
                                       _stream(stream)), "fp4_transcode_mx_to_nv")
     return nv, g, cnt

@@ -9,8 +9,9 @@
 // library's reading (the pages do not print theirs).
 //
 // Pure integer work, bound by HBM: pass 1 reduces the largest exponent of each
-// matrix (one block per matrix, 16-byte loads); pass 2 maps 16 E8M0 bytes to
-// 32 E4M3 bytes per thread and counts blocks with one integer atomic per wave.
+// matrix (one block per matrix, 16-byte loads) and writes the block count;
+// pass 2 maps 16 E8M0 bytes to 32 E4M3 bytes per thread and counts the rare
+// all-zero / re-rounded / NaN blocks with integer atomics.
 #include "common.h"
 
 namespace moe {
@@ -20,20 +21,34 @@ constexpr int kTcThreads = 256;
 __global__ __launch_bounds__(kTcThreads) void transcode_emax(const uint8_t* __restrict__ mx, int64_t per_mat,
                                                              float* __restrict__ gscale,
                                                              int64_t* __restrict__ counters) {
-  if (blockIdx.x == 0 && threadIdx.x < 4) counters[threadIdx.x] = 0;   // zeroed before pass 2 runs
+  // counters: the block count is known (one E8M0 byte per block); the others
+  // start at zero before pass 2 adds to them
+  if (blockIdx.x == 0 && threadIdx.x < 4) counters[threadIdx.x] = threadIdx.x == 0 ? (int64_t)gridDim.x * per_mat : 0;
   const uint8_t* p = mx + (int64_t)blockIdx.x * per_mat;
   int best = -1;                         // largest finite byte (0..254), -1 if none
-  for (int64_t i = (int64_t)threadIdx.x * 16; i < per_mat; i += kTcThreads * 16) {
-    u32x4 v = *(const u32x4*)(p + i);
+  auto take = [&](const u32x4& v) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        int x = (v[j] >> (8 * b)) & 0xFF;
-        if (x != 0xFF && x > best) best = x;
+        const int x = (v[j] >> (8 * b)) & 0xFF;
+        best = (x != 0xFF && x > best) ? x : best;
       }
     }
+  };
+  // whole sweeps with 8 independent 16-byte loads in flight per thread, then
+  // the remainder with single loads (every offset < per_mat)
+  constexpr int kU = 8;
+  constexpr int64_t kSweep = (int64_t)kTcThreads * 16 * kU;
+  const int64_t full = (per_mat / kSweep) * kSweep;
+  for (int64_t s0 = 0; s0 < full; s0 += kSweep) {
+    u32x4 v[kU];
+#pragma unroll
+    for (int q = 0; q < kU; ++q) v[q] = *(const u32x4*)(p + s0 + (int64_t)threadIdx.x * 16 + q * kTcThreads * 16);
+#pragma unroll
+    for (int q = 0; q < kU; ++q) take(v[q]);
   }
+  for (int64_t i = full + (int64_t)threadIdx.x * 16; i < per_mat; i += kTcThreads * 16) take(*(const u32x4*)(p + i));
   __shared__ int wbest[kTcThreads / kWave];
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) best = max(best, __shfl_xor(best, off, kWave));
@@ -64,7 +79,7 @@ __global__ __launch_bounds__(kTcThreads) void transcode_map(const uint8_t* __res
                                                             int64_t per_mat, const float* __restrict__ gscale,
                                                             uint8_t* __restrict__ nv, int64_t* __restrict__ counters) {
   int64_t i = (int64_t)blockIdx.x * kTcThreads + threadIdx.x;   // 16 E8M0 bytes each
-  uint32_t c_zero = 0, c_rr = 0, c_nan = 0, c_blk = 0;
+  uint32_t c_zero = 0, c_rr = 0, c_nan = 0;
   if (i < total16) {
     int64_t off = i * 16;
     int64_t mat = off / per_mat;
@@ -104,21 +119,21 @@ __global__ __launch_bounds__(kTcThreads) void transcode_map(const uint8_t* __res
     u32x4 w1 = {outw[4], outw[5], outw[6], outw[7]};
     *(u32x4*)(nv + off * 2) = w0;
     *(u32x4*)(nv + off * 2 + 16) = w1;
-    c_blk = 16;
   }
-  // one atomic per wave and counter (integer sums: exact in any order)
+  // the rare special blocks: one atomic per wave that has any (integer sums,
+  // exact in any order); the common case issues none
+  if (__ballot(c_zero | c_rr | c_nan) != 0) {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    c_zero += __shfl_xor(c_zero, o, kWave);
-    c_rr += __shfl_xor(c_rr, o, kWave);
-    c_nan += __shfl_xor(c_nan, o, kWave);
-    c_blk += __shfl_xor(c_blk, o, kWave);
-  }
-  if ((threadIdx.x & 63) == 0) {
-    if (c_blk) atomicAdd((unsigned long long*)&counters[0], (unsigned long long)c_blk);
-    if (c_zero) atomicAdd((unsigned long long*)&counters[1], (unsigned long long)c_zero);
-    if (c_rr) atomicAdd((unsigned long long*)&counters[2], (unsigned long long)c_rr);
-    if (c_nan) atomicAdd((unsigned long long*)&counters[3], (unsigned long long)c_nan);
+    for (int o = 32; o >= 1; o >>= 1) {
+      c_zero += __shfl_xor(c_zero, o, kWave);
+      c_rr += __shfl_xor(c_rr, o, kWave);
+      c_nan += __shfl_xor(c_nan, o, kWave);
+    }
+    if ((threadIdx.x & 63) == 0) {
+      if (c_zero) atomicAdd((unsigned long long*)&counters[1], (unsigned long long)c_zero);
+      if (c_rr) atomicAdd((unsigned long long*)&counters[2], (unsigned long long)c_rr);
+      if (c_nan) atomicAdd((unsigned long long*)&counters[3], (unsigned long long)c_nan);
+    }
   }
 }
 
