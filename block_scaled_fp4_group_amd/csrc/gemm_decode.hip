@@ -260,6 +260,15 @@ __device__ __forceinline__ void stage_rows(const GemmArgs& p, uint8_t* lds, int 
 #ifndef MOE_DEC_PF1
 #define MOE_DEC_PF1 4
 #endif
+#ifndef MOE_DEC_NT2
+#define MOE_DEC_NT2 2          // 16-row tiles per wave, gate/up
+#endif
+#ifndef MOE_DEC_NWN1
+#define MOE_DEC_NWN1 8         // waves per workgroup when many waves stream: one matrix (down)
+#endif
+#ifndef MOE_DEC_NWN2
+#define MOE_DEC_NWN2 4         // ... gate/up
+#endif
 __host__ __device__ constexpr int decode_rows_per_pass(int K) { return K > 2048 ? MOE_DEC_MR_4096 : MOE_DEC_MR_2048; }
 __host__ __device__ constexpr int decode_pitch(int K) { return K * 2 + 16; }
 
@@ -407,7 +416,7 @@ static void launch_decode_t(const GemmArgs& a, int wf, bool a_nv, int nact, hipS
 template <int NMAT, int NWN, int KS>
 static void launch_decode_k(const GemmArgs& a, int wf, bool a_nv, int nact, hipStream_t stream) {
   const int nsteps = a.K / 128;
-  constexpr int NT = (KS > 1 || NMAT == 1) ? 1 : 2;
+  constexpr int NT = (KS > 1 || NMAT == 1) ? 1 : MOE_DEC_NT2;
   if (KS == 1 && a.N % (16 * NWN * NT) == 0) {
     if (nsteps == 32) return launch_decode_t<NMAT, NWN, KS, NT, 32>(a, wf, a_nv, nact, stream);
     if (nsteps == 16) return launch_decode_t<NMAT, NWN, KS, NT, 16>(a, wf, a_nv, nact, stream);
@@ -426,7 +435,9 @@ static void launch_decode_ks(const GemmArgs& a, int wf, bool a_nv, int nact, hip
   if (a.N % 64 != 0) {
     launch_decode_k<NMAT, 1, 1>(a, wf, a_nv, nact, stream);
   } else if (waves >= 2048 || nsteps % 8 != 0) {
-    launch_decode_k<NMAT, 4, 1>(a, wf, a_nv, nact, stream);
+    constexpr int NWN = NMAT == 1 ? MOE_DEC_NWN1 : MOE_DEC_NWN2;
+    if (a.N % (16 * NWN) == 0) launch_decode_k<NMAT, NWN, 1>(a, wf, a_nv, nact, stream);
+    else launch_decode_k<NMAT, 4, 1>(a, wf, a_nv, nact, stream);
   } else if (waves >= 1024 || nsteps % 16 != 0) {
     launch_decode_k<NMAT, 2, 2>(a, wf, a_nv, nact, stream);
   } else {
