@@ -157,8 +157,15 @@ __device__ __forceinline__ int pf_lrow(int wn, int g) {
 // One step from an LDS stage into acc[weight group][token group].  WF: weight
 // scale format -- 0 MXFP4, 1 NVFP4 with power-of-two scales (the exact MXFP4
 // transcode), 2 NVFP4 with any E4M3 scales (converted through float).
-template <int NMAT, int WF>
-__device__ __forceinline__ void pf_compute(const uint8_t* st, f32x4 (&acc)[4][4], int wm, int wn, int li, int lg) {
+struct PfNoHook {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
+// hook(s) runs at the start of k-slot s (the direct-to-LDS kernel issues part
+// of the next stage's loads there, between MFMAs).
+template <int NMAT, int WF, typename Hook = PfNoHook>
+__device__ __forceinline__ void pf_compute(const uint8_t* st, f32x4 (&acc)[4][4], int wm, int wn, int li, int lg,
+                                           Hook&& hook = Hook()) {
   constexpr bool W_NV = WF != 0;
   const uint8_t* sa = st;
   const uint8_t* sw = st + kPfAStage;
@@ -186,7 +193,14 @@ __device__ __forceinline__ void pf_compute(const uint8_t* st, f32x4 (&acc)[4][4]
   read_bt(bt[0], 0);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    if (s < 3) read_bt(bt[(s + 1) & 1], s + 1);
+    if (s < 3) {
+      read_bt(bt[(s + 1) & 1], s + 1);
+      // keep the next slot's reads above this slot's MFMAs (the scheduler
+      // would otherwise sink them and reuse one register set)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    hook(s);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const float sc = s < 2 ? s_lo[g] : s_hi[g];
@@ -272,43 +286,52 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_dma_kernel(GemmArgs p
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) wglob[m] = W_NV ? p.w_global[m][T.e] : 1.0f;
 
-    // per-lane sources of this wave's loads; LDS slot = wave base + lane * size
+    // per-lane sources of this wave's loads as 32-bit offsets from uniform
+    // bases (scalar registers); LDS slot = wave base + lane * size
     // tokens: load i fills rows 4 * (4 wv + i) .. +3, lane -> (row, slot lane % 16)
-    const uint8_t* a_src[4];
+    uint32_t a_off[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = (wv * 4 + i) * 4 + (lane >> 4);
       const int chunk = (lane & 15) ^ (row & 15);
       const int64_t r = T.rbase + min(row, T.mrows - 1);            // rows past the tile's end reread a valid row
       const int64_t src = p.gather ? (int64_t)(p.gather[r] / p.gather_div) : r;
-      a_src[i] = p.a_data + src * (int64_t)K * 2 + chunk * 16;
+      a_off[i] = (uint32_t)(src * (int64_t)K * 2) + (uint32_t)chunk * 16u;   // < 2 GiB (checked on the host)
     }
     // weight codes: load j fills rows 16 * (2 wv + j) .. +15 (matrix wv / 4 for SwiGLU)
-    const uint8_t* w_src[2];
     const int wmat = NMAT == 2 ? (wv >> 2) : 0;
+    const uint8_t* w_base = p.w_packed[wmat] + T.e * mat_codes;
+    uint32_t w_off[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int n = (wv * 2 + j) * 16 + (lane >> 2);
       const int chunk = (lane & 3) ^ swz_w_key(n);
-      w_src[j] = p.w_packed[wmat] + T.e * mat_codes + (int64_t)(T.nbase + pf_wrow<NMAT>(n)) * (K / 2) + chunk * 16;
+      w_off[j] = (uint32_t)(T.nbase + pf_wrow<NMAT>(n)) * (uint32_t)(K / 2) + (uint32_t)chunk * 16u;
     }
     // scales: MX rows 64 (wv % 4) + lane (waves 4..7 write an unread copy); NV row 32 wv + lane / 2, half lane % 2
     const int s_n = W_NV ? wv * 32 + (lane >> 1) : (wv & 3) * 64 + lane;
     const int smat = NMAT == 2 ? (W_NV ? (wv >> 2) : ((wv >> 1) & 1)) : 0;
-    const uint8_t* s_src = p.w_scale[smat] + T.e * mat_scales + (int64_t)(T.nbase + pf_wrow<NMAT>(s_n)) * sc_row +
-                           (W_NV ? (lane & 1) * 4 : 0);
+    const uint8_t* s_base = p.w_scale[smat] + T.e * mat_scales;
+    const uint32_t s_off = (uint32_t)(T.nbase + pf_wrow<NMAT>(s_n)) * sc_row + (W_NV ? (lane & 1) * 4 : 0);
 
-    auto issue = [&](auto S_tag, int kb) {
+    // load q (0..6) of step kb into stage S: 4 token loads, 2 weight-code loads, 1 scale load
+    auto issue_one = [&](auto S_tag, int kb, int q) {
       uint8_t* st = pf_stage<decltype(S_tag)::value>();
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(a_src[i] + kb * 256), (lds_void_t*)(st + (wv * 4 + i) * 1024), 16, 0, 0);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        __builtin_amdgcn_global_load_lds((const void*)(w_src[j] + kb * 64), (lds_void_t*)(st + kPfAStage + (wv * 2 + j) * 1024),
+      if (q < 4) {
+        __builtin_amdgcn_global_load_lds((const void*)(p.a_data + kb * 256 + a_off[q]), (lds_void_t*)(st + (wv * 4 + q) * 1024),
                                          16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(s_src + kb * (W_NV ? 8 : 4)),
-                                       (lds_void_t*)(st + kPfAStage + kPfWStage + wv * 256), 4, 0, 0);
+      } else if (q < 6) {
+        const int j = q - 4;
+        __builtin_amdgcn_global_load_lds((const void*)(w_base + kb * 64 + w_off[j]),
+                                         (lds_void_t*)(st + kPfAStage + (wv * 2 + j) * 1024), 16, 0, 0);
+      } else {
+        __builtin_amdgcn_global_load_lds((const void*)(s_base + kb * (W_NV ? 8 : 4) + s_off),
+                                         (lds_void_t*)(st + kPfAStage + kPfWStage + wv * 256), 4, 0, 0);
+      }
+    };
+    auto issue = [&](auto S_tag, int kb) {
+#pragma unroll
+      for (int q = 0; q < kDmaPerStep; ++q) issue_one(S_tag, kb, q);
     };
 
     f32x4 acc[4][4];
@@ -326,9 +349,19 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_dma_kernel(GemmArgs p
       __builtin_amdgcn_s_waitcnt((kDmaPerStep & 15) | (7 << 4) | (15 << 8));      // vmcnt(7)
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      issue(std::integral_constant<int, (S + 2) % 3>(), min(k + 2, nk - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      if (active) pf_compute<NMAT, WF>(pf_stage<S>(), acc, wm, wn, li, lg);
+      const int kn = min(k + 2, nk - 1);
+      constexpr auto SN = std::integral_constant<int, (S + 2) % 3>();
+      // the next stage's loads go out between this step's MFMA slots (two per
+      // slot), so the load unit drains them while the matrix cores work
+      auto hook = [&](int s) {
+        issue_one(SN, kn, 2 * s);
+        if (2 * s + 1 < kDmaPerStep) issue_one(SN, kn, 2 * s + 1);
+      };
+      if (active) {
+        pf_compute<NMAT, WF>(pf_stage<S>(), acc, wm, wn, li, lg, hook);
+      } else {
+        issue(SN, kn);
+      }
     };
 
     __syncthreads();                                                 // previous tile done with the stages
