@@ -97,6 +97,38 @@ def time_steps(layers, inputs, steps, warmup, algo=0, ev_name="gate_up"):
     return total / steps, k_ms
 
 
+def graph_steps(layers, inputs, steps, warmup):
+    """The same steps as time_steps, each layer's forward captured once in a HIP
+    graph and replayed (inputs are the captured buffers).  Returns ms per step."""
+    import torch
+    x, l, b, r = inputs[0]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for ly in layers:
+            ly.forward(x, l, b, r)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for ly in layers:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            ly.forward(x, l, b, r)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    n = len(graphs)
+    for i in range(warmup):
+        graphs[i % n].replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        graphs[i % n].replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
 def distinct_experts(layer, T):
     off = layer.offsets.cpu().numpy()
     return int(np.sum(np.diff(off) > 0))
@@ -168,18 +200,19 @@ def main():
     lws = [make_weights(W) for W in Ws]
     torch.cuda.synchronize()
 
-    def decode_line(T, steps, warmup):
+    def decode_line(T, steps, warmup, graph=False):
         x = synth.activations(wd, T)
         l = synth.logits(wd, T)
         inputs = [(dev_bf16(x), dev(l), None, None)]
         layers = [layer_for(moe, lw, s, T) for lw in lws]
         ms, k_ms = time_steps(layers, inputs, steps, warmup)
+        g_ms = graph_steps(layers, inputs, steps, warmup) if graph else None
         Ds = []
         for ly in layers:
             ly.forward(*inputs[0])
             Ds.append(distinct_experts(ly, T))
         D = float(np.mean(Ds))
-        return dict(T=T, ms=ms, gate_up_ms=k_ms, D=D, x=x, l=l, layers=layers)
+        return dict(T=T, ms=ms, gate_up_ms=k_ms, graph_ms=g_ms, D=D, x=x, l=l, layers=layers)
 
     log("[bench] decode T=64 (headline)")
     main_r = decode_line(64, args.steps, args.warmup)
@@ -219,9 +252,11 @@ def main():
     if not args.no_extras:
         for Tx in (1, 8):
             log(f"[bench] decode T={Tx}")
-            r = decode_line(Tx, max(args.steps, 50), args.warmup)
+            r = decode_line(Tx, max(args.steps, 50), args.warmup, graph=True)
             b = layer_bytes(r["D"], Tx, s)
             extras[f"decode_T{Tx}"] = {"tokens_per_s": round(Tx / (r["ms"] / 1e3), 1), "ms_per_step": round(r["ms"], 4),
+                                       "hip_graph_ms_per_step": round(r["graph_ms"], 4),
+                                       "hip_graph_tokens_per_s": round(Tx / (r["graph_ms"] / 1e3), 1),
                                        "distinct_experts": r["D"],
                                        "layer_hbm_frac": round(b / (r["ms"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                                        "gate_up_hbm_frac": round(gate_up_bytes(r["D"], Tx, s) / (r["gate_up_ms"] / 1e3)

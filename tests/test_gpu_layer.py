@@ -137,6 +137,44 @@ def test_decode_layer(decode_weights, T, sample):
     check_layer(synth.WORKLOADS["decode"], T, W, "mx", "bf16", sample, dev_weights=dw, cache=cache)
 
 
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_decode_layer_hip_graph(decode_weights, T):
+    """The decode layer captured in a HIP graph: every replay (with new inputs
+    copied into the captured buffers, eager work and synchronisations between
+    the replays) gives the same bytes as an eager forward on the same input."""
+    _, dw, _ = decode_weights
+    w = synth.WORKLOADS["decode"]
+    s = w.shape
+    layer = moe.MoELayer(dw, s.num_experts, s.n_group, s.topk_group, s.top_k, s.routed_scaling_factor, T)
+    x_static = dev_bf16(synth.activations(w, T))
+    l_static = dev_f32(synth.logits(w, T))
+    y_static = torch.empty((T, s.hidden), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                        # warm-up off the default stream, as capture requires
+        layer.forward(x_static, l_static, y=y_static)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer.forward(x_static, l_static, y=y_static)
+    torch.cuda.synchronize()
+    eager = moe.MoELayer(dw, s.num_experts, s.n_group, s.topk_group, s.top_k, s.routed_scaling_factor, T)
+    rng = np.random.default_rng(7)
+    for rep in range(4):
+        say(f"graph replay T={T} rep={rep}")
+        xb = synth.bf16_bits_from_f32(rng.standard_normal((T, s.hidden)).astype(np.float32))
+        lg = rng.standard_normal((T, s.num_experts)).astype(np.float32)
+        x_new, l_new = dev_bf16(xb), dev_f32(lg)
+        x_static.copy_(x_new)
+        l_static.copy_(l_new)
+        graph.replay()
+        torch.cuda.synchronize()
+        y_ref = host_bf16_bits(eager.forward(x_new, l_new)).copy()
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bf16_bits(y_static), y_ref), f"replay {rep} differs from eager"
+
+
 def test_decode_mx_equals_nv_bitwise(decode_weights):
     """W4A16 on MX weights and on their NV transcode give identical bytes."""
     W, dw, _ = decode_weights
