@@ -44,7 +44,7 @@ def log(*a):
 def kernel_source_hash():
     import hashlib
     h = hashlib.sha256()
-    for f in ("gemm_decode.hip", "gemm_common.h", "common.h"):
+    for f in ("gemm_decode.h", "gemm_decode.hip", "gemm_decode_tiled.hip", "gemm_common.h", "common.h"):
         with open(os.path.join(ROOT, "block_scaled_fp4_group_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -60,12 +60,17 @@ def dev_bf16(bits):
     return dev(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
 
 
-def make_weights(W):
+TILED = True                   # weights prepared once in the kernels' tiled layout (--row-major: off)
+
+
+def make_weights(W, tiled=None):
     import block_scaled_fp4_group_amd as moe
+    tiled = TILED if tiled is None else tiled
 
     def one(name):
         p, s = W[name][0], W[name][1]
-        return moe.Weights(dev(p), dev(s))
+        w = moe.Weights(dev(p), dev(s))
+        return moe.tile_weights(w) if tiled else w
     return moe.LayerWeights(one("gate"), one("up"), one("down"))
 
 
@@ -169,10 +174,14 @@ def main():
     ap.add_argument("--rotate", type=int, default=4, help="independent decode weight sets")
     ap.add_argument("--no-extras", action="store_true", help="only the headline decode line")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--row-major", action="store_true",
+                    help="keep the weights in their row-major layout (default: tiled once before timing)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes) and exit")
     args = ap.parse_args()
+    global TILED
+    TILED = not args.row_major
     if args.copy_calibration:
         import torch
         n = args.copy_calibration << 20
@@ -239,11 +248,12 @@ def main():
         "config": {"workload": "decode W4A16 MXFP4: 256 experts (8 groups, keep 4, top-8, scale 2.827), "
                                "hidden 4096, expert intermediate 2048, 64 tokens, 4 rotated weight sets",
                    "tokens": T, "experts": 256, "hidden": 4096, "intermediate": 2048, "top_k": 8,
-                   "weights": "MXFP4", "activations": "bf16", "distinct_experts": main_r["D"]},
+                   "weights": "MXFP4, " + ("tiled layout" if TILED else "row-major"), "activations": "bf16",
+                   "distinct_experts": main_r["D"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if tr is None else tr,
-                     "kernel": "gemm_decode_kernel (gate/up + SwiGLU)",
+                     "kernel": "gemm_decode_kernel (gate/up + SwiGLU" + (", tiled weights)" if TILED else ")"),
                      "kernel_ms": round(main_r["gate_up_ms"], 5),
                      "algorithmic_bytes": int(gu_bytes)},
         "layer_hbm_frac": round(lb / (main_r["ms"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -262,7 +272,7 @@ def main():
                                        "gate_up_hbm_frac": round(gate_up_bytes(r["D"], Tx, s) / (r["gate_up_ms"] / 1e3)
                                                                  / 1e9 / HBM_PEAK_GBS, 4)}
             del r
-        extras.update(prefill_lines(moe, synth, lws, args))
+        extras.update(prefill_lines(moe, synth, Ws[0], args))
     out["extras"] = extras
     if not args.no_cpu:
         log("[bench] CPU oracle baseline")
@@ -275,7 +285,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def prefill_lines(moe, synth, decode_lws, args):
+def prefill_lines(moe, synth, decode_W, args):
     """MFMA-bound shapes: prefill (T=8192, biased routing), W4A4 (T=4096 on the
     NVFP4 transcode of the decode weights) and REAP-50 (128 experts, 2 layers)."""
     import torch
@@ -305,7 +315,7 @@ def prefill_lines(moe, synth, decode_lws, args):
 
     log("[bench] W4A4 T=4096")
     ww = synth.WORKLOADS["w4a4"]
-    src = decode_lws[0]
+    src = make_weights(decode_W, tiled=False)    # the transcode reads the row-major MXFP4 tensors
     nvw = {}
     tc_ms = []
     for name in ("gate", "up", "down"):
@@ -323,6 +333,8 @@ def prefill_lines(moe, synth, decode_lws, args):
         tc_ms.append(e0.elapsed_time(e1))
         assert int(cnt[2].item()) == 0
         nvw[name] = moe.Weights(t.packed, sc, g, scales_pow2=True)    # the transcode's scales are powers of two
+        if TILED:
+            nvw[name] = moe.tile_weights(nvw[name])
     E = ww.shape.num_experts
     tc_bytes = 3 * E * 2048 * 4096 * (1 / 32 + 2 / 16)      # read E8M0, write 2x E4M3
     T = 4096
@@ -335,7 +347,7 @@ def prefill_lines(moe, synth, decode_lws, args):
                          "mfma_frac_bf16": round(mfma_frac(T, ms), 4),
                          "fp4_peak_frac": round(mfma_frac(T, ms) * BF16_PEAK_TFLOPS / FP4_PEAK_TFLOPS, 4),
                          "transcode_GBs": round(tc_bytes / (sum(tc_ms) / 1e3) / 1e9, 1)}
-    del ly, lw4, nvw
+    del ly, lw4, nvw, src
     torch.cuda.empty_cache()
 
     log("[bench] REAP-50 T=16384, 2 layers")

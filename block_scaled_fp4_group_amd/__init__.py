@@ -18,13 +18,14 @@ LIB_PATH = os.path.join(_PKG, "libmoefp4.so")
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, 1, 2, 3, 4
 MOE_FP4_MX, MOE_FP4_NV = 0, 1
-MOE_FP4_SCALES_POW2 = 1
+MOE_FP4_SCALES_POW2, MOE_FP4_TILED = 1, 2
 MOE_ACT_BF16, MOE_ACT_NVFP4 = 0, 1
 MOE_EPI_NONE, MOE_EPI_SWIGLU = 0, 1
-MOE_ALGO_AUTO, MOE_ALGO_DECODE, MOE_ALGO_PREFILL = 0, 1, 2
+MOE_ALGO_AUTO, MOE_ALGO_DECODE, MOE_ALGO_PREFILL, MOE_ALGO_DECODE_PERSISTENT = 0, 1, 2, 3
 
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_version", "moe_route", "moe_permute_workspace_bytes",
-           "moe_permute", "moe_fp4_grouped_gemm", "moe_combine", "fp4_transcode_mx_to_nv", "moe_quantize_nvfp4")
+           "moe_permute", "moe_fp4_grouped_gemm", "moe_combine", "fp4_transcode_mx_to_nv", "moe_quantize_nvfp4",
+           "moe_fp4_tile_weights")
 
 
 class RouteParams(ctypes.Structure):
@@ -76,6 +77,8 @@ def _load() -> ctypes.CDLL:
     lib.fp4_transcode_mx_to_nv.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp, vp]
     lib.moe_quantize_nvfp4.restype = i32
     lib.moe_quantize_nvfp4.argtypes = [vp, i64, i32, f32, vp, vp, vp, vp]
+    lib.moe_fp4_tile_weights.restype = i32
+    lib.moe_fp4_tile_weights.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
     return lib
 
 
@@ -150,6 +153,7 @@ class Weights:
     scale: torch.Tensor                   # u8 [E, n, k/32] (MX) | [E, n, k/16] (NV)
     global_scale: Optional[torch.Tensor] = None   # f32 [E] (NV)
     scales_pow2: bool = False             # NV: every scale byte is 0 or a power of two (a transcode)
+    tiled: bool = False                   # codes and scales in the tiled layout (see tile_weights)
 
     @property
     def format(self):
@@ -159,7 +163,7 @@ class Weights:
         E, n, k2 = self.packed.shape
         return Fp4Weights(self.format, E, n, 2 * k2, self.packed.data_ptr(), self.scale.data_ptr(),
                           None if self.global_scale is None else self.global_scale.data_ptr(),
-                          MOE_FP4_SCALES_POW2 if self.scales_pow2 else 0)
+                          (MOE_FP4_SCALES_POW2 if self.scales_pow2 else 0) | (MOE_FP4_TILED if self.tiled else 0))
 
 
 def grouped_gemm(a: torch.Tensor, w0: Weights, w1: Optional[Weights], offsets: torch.Tensor, rows: int,
@@ -211,6 +215,18 @@ def transcode_mx_to_nv(mx_scale: torch.Tensor, packed: torch.Tensor, nv=None, g=
     _check(lib.fp4_transcode_mx_to_nv(_ptr(mx_scale), _ptr(packed), M, n, k, _ptr(nv), _ptr(g), _ptr(cnt),
                                       _stream(stream)), "fp4_transcode_mx_to_nv")
     return nv, g, cnt
+
+
+def tile_weights(w: Weights, stream=None) -> Weights:
+    """Copy of ``w`` in the tiled layout (same values; shapes unchanged, flag MOE_FP4_TILED)."""
+    if w.tiled:
+        return w
+    E, n, k2 = w.packed.shape
+    packed = torch.empty_like(w.packed)
+    scale = torch.empty_like(w.scale)
+    _check(lib.moe_fp4_tile_weights(w.format, E, n, 2 * k2, _ptr(w.packed), _ptr(w.scale), _ptr(packed), _ptr(scale),
+                                    _stream(stream)), "moe_fp4_tile_weights")
+    return Weights(packed, scale, w.global_scale, w.scales_pow2, tiled=True)
 
 
 def quantize_nvfp4(x: torch.Tensor, input_scale: float = 1.0, codes=None, scales=None, dequant=None, stream=None):

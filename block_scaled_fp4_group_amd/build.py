@@ -1,9 +1,13 @@
 """Build the gfx950 shared library in-tree with hipcc (no torch involved).
 
     python -m block_scaled_fp4_group_amd.build
+
+Each HIP source compiles to its own object in parallel (the GEMM files hold
+many kernel instantiations), then one link step writes libmoefp4.so.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import glob
 import os
 import subprocess
@@ -12,6 +16,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libmoefp4.so")
+OBJ_DIR = os.path.join(PKG, "_build")
 ARCH = "gfx950"
 
 
@@ -22,28 +27,51 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def command(out: str = LIB) -> list:
-    srcs = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
-    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+def sources() -> list:
+    return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
+
+
+def compile_command(src: str, obj: str) -> list:
+    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-c",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-Wno-unused-command-line-argument",
-            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
-            *srcs, "-o", out]
+            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"), src, "-o", obj]
 
 
-def build(verbose: bool = True) -> str:
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def link_command(objs: list, out: str) -> list:
+    return [hipcc(), f"--offload-arch={ARCH}", "-fPIC", "-shared", *objs, "-o", out]
+
+
+def _run(cmd: list) -> tuple:
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l and l.strip()]
-    if r.returncode != 0:
+    return r.returncode, msgs
+
+
+def build(verbose: bool = True, jobs: int = 0) -> str:
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    srcs = sources()
+    objs = [os.path.join(OBJ_DIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    jobs = jobs or max(1, min(len(srcs), os.cpu_count() or 4, 16))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        results = list(ex.map(_run, [compile_command(s, o) for s, o in zip(srcs, objs)]))
+    failed = False
+    for src, (rc, msgs) in zip(srcs, results):
+        if rc != 0:
+            failed = True
+            sys.stderr.write(f"hipcc failed on {os.path.basename(src)}:\n" + "\n".join(msgs) + "\n")
+        elif msgs and verbose:
+            print("\n".join(msgs))
+    if failed:
+        raise RuntimeError("hipcc failed")
+    tmp = LIB + ".tmp"
+    rc, msgs = _run(link_command(objs, tmp))
+    if rc != 0:
         sys.stderr.write("\n".join(msgs) + "\n")
-        raise RuntimeError(f"hipcc failed with exit code {r.returncode}")
-    if msgs and verbose:
-        print("\n".join(msgs))
+        raise RuntimeError(f"link failed with exit code {rc}")
     os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB} from {len(srcs)} sources", flush=True)
     return LIB
 
 

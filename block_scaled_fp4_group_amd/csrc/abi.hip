@@ -31,7 +31,8 @@ moe_status launch_permute(const int32_t*, int64_t, int, int, int32_t*, int32_t*,
 moe_status launch_combine(const void*, const int32_t*, const float*, const void*, int64_t, int, int, void*, hipStream_t);
 moe_status launch_transcode(const uint8_t*, const uint8_t*, int64_t, int, int, uint8_t*, float*, int64_t*, hipStream_t);
 moe_status launch_quant(const void*, int64_t, int, float, uint8_t*, uint8_t*, void*, hipStream_t);
-moe_status launch_gemm_decode(const GemmArgs&, bool swiglu, int wf, bool a_nv, int64_t rows, hipStream_t);
+moe_status launch_tile(bool, int64_t, int, int, const uint8_t*, const uint8_t*, uint8_t*, uint8_t*, hipStream_t);
+moe_status launch_gemm_decode(const GemmArgs&, bool swiglu, int wf, bool a_nv, int64_t rows, int persistent, hipStream_t);
 moe_status launch_gemm_prefill(const GemmArgs&, bool swiglu, int wf, bool a_nv, int64_t rows, hipStream_t);
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -120,10 +121,15 @@ static moe_status check_weights(const moe_fp4_weights* w, const char* name) {
   MOE_CHECK(w->packed && w->scale, "moe_fp4_grouped_gemm: %s NULL data", name);
   MOE_CHECK(aligned16(w->packed), "moe_fp4_grouped_gemm: %s codes not 16-byte aligned", name);
   if (w->format == MOE_FP4_NV) MOE_CHECK(w->global_scale != nullptr, "moe_fp4_grouped_gemm: %s NV without global", name);
-  MOE_CHECK((w->flags & ~MOE_FP4_SCALES_POW2) == 0, "moe_fp4_grouped_gemm: %s unknown flags 0x%x", name, w->flags);
+  MOE_CHECK((w->flags & ~(MOE_FP4_SCALES_POW2 | MOE_FP4_TILED)) == 0, "moe_fp4_grouped_gemm: %s unknown flags 0x%x",
+            name, w->flags);
   if (w->k % 128 != 0 || w->n % 16 != 0) {
     set_error("moe_fp4_grouped_gemm: %s needs k %% 128 == 0 and n %% 16 == 0 (n=%d k=%d)", name, w->n, w->k);
     return MOE_ERR_UNSUPPORTED;
+  }
+  if (w->flags & MOE_FP4_TILED) {
+    MOE_CHECK(w->k % 512 == 0, "moe_fp4_grouped_gemm: %s tiled layout needs k %% 512 == 0 (k=%d)", name, w->k);
+    MOE_CHECK(aligned16(w->scale), "moe_fp4_grouped_gemm: %s tiled scales not 16-byte aligned", name);
   }
   return MOE_OK;
 }
@@ -162,7 +168,7 @@ moe_status moe_fp4_grouped_gemm(const moe_act* a, const moe_fp4_weights* w0, con
   if (out->codes) MOE_CHECK(out->scales != nullptr, "moe_fp4_grouped_gemm: NVFP4 output needs scales");
   if (out->codes || out->dequant)
     MOE_CHECK(is_pow2_float(out->output_scale), "moe_fp4_grouped_gemm: output_scale must be a power of two");
-  MOE_CHECK(algo >= MOE_ALGO_AUTO && algo <= MOE_ALGO_PREFILL, "moe_fp4_grouped_gemm: bad algo");
+  MOE_CHECK(algo >= MOE_ALGO_AUTO && algo <= MOE_ALGO_DECODE_PERSISTENT, "moe_fp4_grouped_gemm: bad algo");
   if (rows == 0) return MOE_OK;
 
   GemmArgs g;
@@ -192,6 +198,7 @@ moe_status moe_fp4_grouped_gemm(const moe_act* a, const moe_fp4_weights* w0, con
   g.out_inv_g = nvfp4_out ? 1.0f / out->output_scale : 1.0f;
   g.out_dq = (uint16_t*)out->dequant;
   g.out_g = nvfp4_out ? out->output_scale : 1.0f;
+  g.tiled = (w0->flags & MOE_FP4_TILED) != 0;
 
   const bool swiglu = epi == MOE_EPI_SWIGLU;
   // weight scale format: 0 MXFP4, 1 NVFP4 with power-of-two scales, 2 NVFP4 with any scales
@@ -200,7 +207,7 @@ moe_status moe_fp4_grouped_gemm(const moe_act* a, const moe_fp4_weights* w0, con
   int use = algo;
   if (use == MOE_ALGO_AUTO) use = (rows >= 32LL * g.E) ? MOE_ALGO_PREFILL : MOE_ALGO_DECODE;
   if (use == MOE_ALGO_PREFILL) return launch_gemm_prefill(g, swiglu, wf, a_nv, rows, stream);
-  return launch_gemm_decode(g, swiglu, wf, a_nv, rows, stream);
+  return launch_gemm_decode(g, swiglu, wf, a_nv, rows, use == MOE_ALGO_DECODE_PERSISTENT, stream);
 }
 
 moe_status moe_combine(const void* expert_out, const int32_t* slot_rows, const float* topk_weights,
@@ -228,6 +235,30 @@ moe_status fp4_transcode_mx_to_nv(const uint8_t* mx_scale, const uint8_t* packed
               "fp4_transcode_mx_to_nv: buffers must be 16-byte aligned");
   }
   return launch_transcode(mx_scale, packed, num_mats, n, k, nv_scale, global_scale, counters, stream);
+}
+
+moe_status moe_fp4_tile_weights(moe_fp4_format format, int32_t num_experts, int32_t n, int32_t k,
+                                const uint8_t* packed, const uint8_t* scale, uint8_t* packed_tiled,
+                                uint8_t* scale_tiled, hipStream_t stream) {
+  g_err[0] = 0;
+  MOE_CHECK(format == MOE_FP4_MX || format == MOE_FP4_NV, "moe_fp4_tile_weights: bad format");
+  MOE_CHECK(num_experts >= 0 && n >= 16 && k >= 512, "moe_fp4_tile_weights: bad sizes");
+  MOE_CHECK(n % 16 == 0 && k % 512 == 0, "moe_fp4_tile_weights: needs n %% 16 == 0 and k %% 512 == 0");
+  if (num_experts == 0) return MOE_OK;
+  MOE_CHECK(packed && scale && packed_tiled && scale_tiled, "moe_fp4_tile_weights: NULL pointer");
+  MOE_CHECK(aligned16(packed) && aligned16(scale) && aligned16(packed_tiled) && aligned16(scale_tiled),
+            "moe_fp4_tile_weights: buffers must be 16-byte aligned");
+  const uint64_t cb = (uint64_t)num_experts * (uint64_t)n * (uint64_t)(k / 2);
+  const uint64_t sb = (uint64_t)num_experts * (uint64_t)n * (uint64_t)(format == MOE_FP4_NV ? k / 16 : k / 32);
+  auto overlap = [](const void* a, uint64_t na, const void* b, uint64_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+  };
+  MOE_CHECK(!overlap(packed, cb, packed_tiled, cb) && !overlap(scale, sb, scale_tiled, sb) &&
+                !overlap(packed, cb, scale_tiled, sb) && !overlap(scale, sb, packed_tiled, cb) &&
+                !overlap(packed_tiled, cb, scale_tiled, sb),
+            "moe_fp4_tile_weights: outputs overlap inputs or each other");
+  return launch_tile(format == MOE_FP4_NV, num_experts, n, k, packed, scale, packed_tiled, scale_tiled, stream);
 }
 
 moe_status moe_quantize_nvfp4(const void* x, int64_t rows, int32_t k, float input_scale, uint8_t* codes,

@@ -26,6 +26,24 @@ struct GemmArgs {
   float out_inv_g;                // 1 / output global scale
   uint16_t* out_dq;               // [rows, N] bf16 NVFP4 values (codes x scale x global) or null
   float out_g;                    // output global scale
+  int tiled;                      // weights in the tiled layout (host-side dispatch)
+};
+
+// Offsets of one wavefront's weight operands.  Lane (li, lg) of a 16-row tile
+// holds row li, code chunk lg of each 128-column step and row li's scales of
+// each 4-step window; the tile's own base and the step / window count are
+// added by the caller (a tile spans 16 * K/2 code bytes and 16 * sc_row scale
+// bytes in either layout).
+template <bool TL, bool W_NV>
+struct WeightLane {
+  static constexpr uint32_t kStep = TL ? 1024u : 64u;                       // code bytes per step
+  static constexpr uint32_t kWin = TL ? (W_NV ? 512u : 256u) : (W_NV ? 32u : 16u);   // scale bytes per window
+  __host__ __device__ static uint32_t code(int li, int lg, int K) {
+    return TL ? (uint32_t)(lg * 16 + li) * 16u : (uint32_t)li * (uint32_t)(K / 2) + (uint32_t)lg * 16u;
+  }
+  __host__ __device__ static uint32_t scale(int li, int K) {
+    return TL ? (uint32_t)li * (W_NV ? 32u : 16u) : (uint32_t)li * (uint32_t)(W_NV ? K / 16 : K / 32);
+  }
 };
 
 // Locate the j-th expert with at least one row (experts in index order).
@@ -65,5 +83,16 @@ __device__ __forceinline__ bool find_active_expert(const int32_t* __restrict__ o
 }
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+
+// compute units of the current device (persistent grids: one workgroup per CU)
+inline int device_cus() {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  }
+  return cus;
+}
 
 }  // namespace moe

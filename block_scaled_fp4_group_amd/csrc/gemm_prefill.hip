@@ -1,562 +1,21 @@
-// Grouped FP4 expert GEMM, MFMA-bound ("prefill") form: many token rows per
-// expert, so the kernel is bound by bf16 MFMA throughput.
-//
-// Same contraction as the weight-streaming kernel (the SwiGLU expert FFN of
-// "MiMo-V2.6-Flash -- REAP-50", "Pruning Method"; MXFP4 / NVFP4 weights with
-// FP32 accumulation, "AxionML / MiMo-V2.6-Flash-MOPD-NVFP4", "About NVFP4
-// quantization"), tiled for reuse:
-//   * a workgroup of 8 waves owns a tile of BM = 128 token rows x BN = 256
-//     weight rows (SwiGLU: 128 gate + 128 up rows of the same outputs) and
-//     walks K in steps of BK = 128;
-//   * each wave dequantises its 64 weight rows from LDS with the gfx950
-//     convert instruction and runs 4 x 4 bf16 16x16x32 MFMA tiles (64 tokens
-//     x 64 weight rows); the token operands of the next k-slot are read while
-//     the current slot's MFMAs run;
-//   * LDS layouts are XOR-swizzled so the MFMA operand reads are conflict
-//     free: token chunk c (16 B) of row r at c ^ (r % 16) in a 256-B row,
-//     weight chunk c of row n at c ^ ((n / 2 ^ n / 8) % 4) in a 64-B row;
-//   * persistent workgroups: the tile list, ordered (expert, n-tile, m-tile),
-//     is cut into one contiguous slice per XCD (workgroup b runs on XCD b % 8),
-//     so the workgroups sharing an L2 work on the same experts' token rows and
-//     weight slices at the same time.
-// Two operand pipelines:
-//   * bf16 tokens: every step's operands go from HBM straight into one of
-//     three LDS stages (direct-to-LDS loads, no registers), two steps ahead;
-//     one barrier per step;
-//   * NVFP4 tokens (W4A4): the token rows must be dequantised on the way in,
-//     so operands are fetched two steps ahead into registers and written to
-//     one of two LDS stages one step ahead.
-#include <algorithm>
-#include <type_traits>
-
-#include "gemm_common.h"
+// Grouped FP4 expert GEMM, MFMA-bound ("prefill") form: entry point and the
+// kernels on row-major weights (kernels in gemm_prefill.h; the tiled-layout
+// variants are instantiated in gemm_prefill_tiled.hip).
+#include "gemm_prefill.h"
 
 namespace moe {
 
-constexpr int kPfBM = 128, kPfBN = 256, kPfBK = 128;
-constexpr int kPfThreads = 512;                          // 8 waves: 2 along tokens x 4 along weight rows
-constexpr int kPfAStage = kPfBM * kPfBK * 2;             // 32 KB of bf16 tokens
-constexpr int kPfWStage = kPfBN * kPfBK / 2;             // 16 KB of FP4 codes
-constexpr int kPfSStage = kPfBN * 8;                     // 2 KB of scales (MX uses 4 B per row)
-constexpr int kPfStage = kPfAStage + kPfWStage + kPfSStage;
-constexpr int kPfMaxE = 1024;
-constexpr int kPfXcds = 8;
+template void prefill_run<false>(const GemmArgs&, bool, int, bool, hipStream_t);
 
-// the three stages of the direct-to-LDS pipeline: separate objects, so the
-// compiler can tell a stage being read from the stages being filled
-__shared__ __attribute__((aligned(16))) uint8_t pf_stage0[kPfStage];
-__shared__ __attribute__((aligned(16))) uint8_t pf_stage1[kPfStage];
-__shared__ __attribute__((aligned(16))) uint8_t pf_stage2[kPfStage];
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-__device__ __forceinline__ uint32_t swz_a(int row, int chunk) { return (uint32_t)(row * 256 + ((chunk ^ (row & 15)) << 4)); }
-// (n / 2 ^ n / 8) % 4 keeps any 8 consecutive rows (one 128-B bank sweep) and
-// any 16 consecutive rows (one 256-B sweep) on distinct 16-B slots
-__device__ __forceinline__ int swz_w_key(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
-__device__ __forceinline__ uint32_t swz_w(int row, int chunk) { return (uint32_t)(row * 64 + ((chunk ^ swz_w_key(row)) << 4)); }
-
-__device__ __forceinline__ uint32_t quant4_lanes(const float* v, float inv_g, uint32_t& sb_out) {
-  float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-  amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
-  amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
-  float target = (amax * inv_g) / 6.0f;
-  uint32_t sb = f32_to_e4m3_sat(target);
-  float s = e4m3_to_f32(sb);
-  uint32_t bits = 0;
-  if (s > 0.0f) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float xs = v[i] * inv_g;
-      bits |= (e2m1_code(fabsf(xs), s) | ((__float_as_uint(xs) >> 28) & 8u)) << (4 * i);
-    }
-  }
-  sb_out = sb;
-  return bits;
-}
-
-// ---------------------------------------------------------------- tiles
-// s_pref[e] = tiles before expert e (expert e owns ceil(rows_e / BM) * ntn tiles)
-template <int NTHR>
-__device__ __forceinline__ int build_tile_table(const GemmArgs& p, int ntn, int* s_pref, int* s_wc) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  int running = 0;
-  for (int e0 = 0; e0 < p.E; e0 += NTHR) {
-    const int e = e0 + tid;
-    int cnt = 0;
-    if (e < p.E) {
-      int r0 = (int)max((int64_t)0, min((int64_t)p.offsets[e], p.rows));
-      int r1 = (int)max((int64_t)r0, min((int64_t)p.offsets[e + 1], p.rows));
-      cnt = ((r1 - r0 + kPfBM - 1) / kPfBM) * ntn;
-    }
-    int x = cnt;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      int y = __shfl_up(x, off, kWave);
-      if (lane >= off) x += y;
-    }
-    if (lane == 63) s_wc[wv] = x;
-    __syncthreads();
-    int before = running;
-    for (int i = 0; i < wv; ++i) before += s_wc[i];
-    if (e < p.E) s_pref[e] = before + x - cnt;
-    int tot = 0;
-    for (int i = 0; i < NTHR / kWave; ++i) tot += s_wc[i];
-    running += tot;
-    __syncthreads();
-  }
-  if (tid == 0) s_pref[p.E] = running;
-  __syncthreads();
-  return s_pref[p.E];
-}
-
-struct PfTile {
-  int e, rbase, mrows, nbase;
-};
-
-// (expert, n-tile, m-tile) of a tile index; the m-tiles of one n-tile are consecutive
-template <int NMAT>
-__device__ __forceinline__ PfTile locate_tile(const GemmArgs& p, const int* s_pref, int tile) {
-  int lo = 0, hi = p.E - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (s_pref[mid] <= tile) lo = mid;
-    else hi = mid - 1;
-  }
-  PfTile t;
-  t.e = lo;
-  const int r0 = (int)max((int64_t)0, min((int64_t)p.offsets[lo], p.rows));
-  const int r1 = (int)max((int64_t)r0, min((int64_t)p.offsets[lo + 1], p.rows));
-  const int mt_cnt = (r1 - r0 + kPfBM - 1) / kPfBM;
-  const int local = tile - s_pref[lo];
-  const int nt = local / mt_cnt, mt = local % mt_cnt;
-  t.rbase = r0 + mt * kPfBM;
-  t.mrows = min(kPfBM, r1 - t.rbase);
-  t.nbase = nt * (kPfBN / NMAT);                                    // first row of each matrix's slab
-  return t;
-}
-
-// this workgroup's share of the tile list: a contiguous slice per XCD
-__device__ __forceinline__ void xcd_slice(int total, int& begin, int& end, int& stride) {
-  const int nx = (gridDim.x % kPfXcds == 0) ? kPfXcds : 1;
-  const int xcd = blockIdx.x % nx, slot = blockIdx.x / nx;
-  stride = gridDim.x / nx;
-  begin = (int)((int64_t)total * xcd / nx) + slot;
-  end = (int)((int64_t)total * (xcd + 1) / nx);
-}
-
-// block-local weight row n (0..255): matrix n / 128 (SwiGLU), row within the slab
-template <int NMAT>
-__device__ __forceinline__ int pf_wrow(int n) { return NMAT == 2 ? (n & 127) : n; }
-// wave (wm, wn)'s weight group g (16 rows): block-local row base
-template <int NMAT>
-__device__ __forceinline__ int pf_lrow(int wn, int g) {
-  return NMAT == 2 ? (g >> 1) * 128 + wn * 32 + (g & 1) * 16 : wn * 64 + g * 16;
-}
-
-// One step from an LDS stage into acc[weight group][token group].  WF: weight
-// scale format -- 0 MXFP4, 1 NVFP4 with power-of-two scales (the exact MXFP4
-// transcode), 2 NVFP4 with any E4M3 scales (converted through float).
-struct PfNoHook {
-  __device__ __forceinline__ void operator()(int) const {}
-};
-
-// hook(s) runs at the start of k-slot s (the direct-to-LDS kernel issues part
-// of the next stage's loads there, between MFMAs).
-template <int NMAT, int WF, typename Hook = PfNoHook>
-__device__ __forceinline__ void pf_compute(const uint8_t* st, f32x4 (&acc)[4][4], int wm, int wn, int li, int lg,
-                                           Hook&& hook = Hook()) {
-  constexpr bool W_NV = WF != 0;
-  const uint8_t* sa = st;
-  const uint8_t* sw = st + kPfAStage;
-  const uint8_t* ss = st + kPfAStage + kPfWStage;
-  u32x4 wq[4];
-  float s_lo[4], s_hi[4];
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int n = pf_lrow<NMAT>(wn, g) + li;
-    wq[g] = *(const u32x4*)(sw + swz_w(n, lg));
-    if (W_NV) {
-      const uint32_t b2 = *(const uint16_t*)(ss + n * 8 + lg * 2);
-      s_lo[g] = e4m3_to_f32(b2 & 0xFF);
-      s_hi[g] = e4m3_to_f32(b2 >> 8);
-    } else {
-      s_lo[g] = s_hi[g] = e8m0_to_f32(ss[n * 4 + lg]);
-    }
-  }
-  bf16x8 bt[2][4];
-  auto read_bt = [&](bf16x8 (&b)[4], int s) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      b[t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(sa + swz_a(wm * 64 + t * 16 + li, lg * 4 + s)));
-  };
-  read_bt(bt[0], 0);
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    if (s < 3) {
-      read_bt(bt[(s + 1) & 1], s + 1);
-      // keep the next slot's reads above this slot's MFMAs (the scheduler
-      // would otherwise sink them and reuse one register set)
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    hook(s);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const float sc = s < 2 ? s_lo[g] : s_hi[g];
-      const bf16x8 af = WF == 2 ? fp4x8_to_bf16_general(wq[g][s], sc) : fp4x8_to_bf16_pow2(wq[g][s], sc);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) acc[g][t] = mfma16(af, bt[s & 1][t], acc[g][t]);
-    }
-  }
-}
-
-// Epilogue: lane holds D[weight row 4*lg + i of group g][token row li of group t].
-template <int NMAT>
-__device__ __forceinline__ void pf_epilogue(const GemmArgs& p, const PfTile& T, const f32x4 (&acc)[4][4],
-                                            const float (&wglob)[NMAT], int wm, int wn, int li, int lg) {
-  const int N = p.N;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int mrow = wm * 64 + t * 16 + li;
-    const bool ok = mrow < T.mrows;
-    const int64_t ro = T.rbase + mrow;
-#pragma unroll
-    for (int gp = 0; gp < (NMAT == 2 ? 2 : 4); ++gp) {
-      float v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float g = acc[gp][t][i] * wglob[0];
-        v[i] = NMAT == 2 ? silu_f(g) * (acc[gp + 2][t][i] * wglob[NMAT - 1]) : g;
-      }
-      const int col = T.nbase + (NMAT == 2 ? wn * 32 + gp * 16 : wn * 64 + gp * 16) + 4 * lg;
-      const uint32_t b01 = pack_bf16x2(v[0], v[1]), b23 = pack_bf16x2(v[2], v[3]);
-      if (p.out_bf16 && ok) *(u32x2*)(p.out_bf16 + ro * N + col) = u32x2{b01, b23};
-      if (p.out_codes || p.out_dq) {
-        float q[4] = {bf16_lo(b01), bf16_hi(b01), bf16_lo(b23), bf16_hi(b23)};
-        uint32_t sb;
-        const uint32_t bits = quant4_lanes(q, p.out_inv_g, sb);
-        if (ok) {
-          if (p.out_codes) {
-            *(uint16_t*)(p.out_codes + ro * (N / 2) + col / 2) = (uint16_t)bits;
-            if (lg == 0) p.out_scales[ro * (N / 16) + (col - 4 * lg) / 16] = (uint8_t)sb;
-          }
-          if (p.out_dq) *(u32x2*)(p.out_dq + ro * N + col) = nvfp4_dequant4(bits, e4m3_to_f32(sb) * p.out_g);
-        }
-      }
-    }
-  }
-}
-
-// ------------------------------------------------ bf16 tokens: direct to LDS
-template <int S>
-__device__ __forceinline__ uint8_t* pf_stage() {
-  return S == 0 ? pf_stage0 : (S == 1 ? pf_stage1 : pf_stage2);
-}
-
-template <int NMAT, int WF>
-__global__ __launch_bounds__(kPfThreads) void gemm_prefill_dma_kernel(GemmArgs p) {
-  constexpr bool W_NV = WF != 0;
-  __shared__ int s_pref[kPfMaxE + 1];
-  __shared__ int s_wc[kPfThreads / kWave];
-  constexpr int kDmaPerStep = 7;                                     // direct-to-LDS loads per wave and step
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wv >> 2, wn = wv & 3;                               // SIMD s holds waves s (wm 0) and s + 4 (wm 1)
-  const int li = lane & 15, lg = lane >> 4;
-  const int K = p.K, N = p.N;
-  const int ntn = N / (kPfBN / NMAT);
-  const int nk = K / kPfBK;
-  const int total = build_tile_table<kPfThreads>(p, ntn, s_pref, s_wc);
-  int t_begin, t_end, t_stride;
-  xcd_slice(total, t_begin, t_end, t_stride);
-
-  const uint32_t sc_row = (uint32_t)(W_NV ? K / 16 : K / 32);
-  const int64_t mat_codes = (int64_t)N * (K / 2);
-  const int64_t mat_scales = (int64_t)N * sc_row;
-
-  for (int tile = t_begin; tile < t_end; tile += t_stride) {
-    const PfTile T = locate_tile<NMAT>(p, s_pref, tile);
-    // a wave whose 64 token rows all lie past the tile's end skips its MFMA
-    // work (its SIMD then runs the other wave alone); it still loads and syncs
-    const bool active = wm * 64 < T.mrows;
-    float wglob[NMAT];
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m) wglob[m] = W_NV ? p.w_global[m][T.e] : 1.0f;
-
-    // per-lane sources of this wave's loads as 32-bit offsets from uniform
-    // bases (scalar registers); LDS slot = wave base + lane * size
-    // tokens: load i fills rows 4 * (4 wv + i) .. +3, lane -> (row, slot lane % 16)
-    uint32_t a_off[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = (wv * 4 + i) * 4 + (lane >> 4);
-      const int chunk = (lane & 15) ^ (row & 15);
-      const int64_t r = T.rbase + min(row, T.mrows - 1);            // rows past the tile's end reread a valid row
-      const int64_t src = p.gather ? (int64_t)(p.gather[r] / p.gather_div) : r;
-      a_off[i] = (uint32_t)(src * (int64_t)K * 2) + (uint32_t)chunk * 16u;   // < 2 GiB (checked on the host)
-    }
-    // weight codes: load j fills rows 16 * (2 wv + j) .. +15 (matrix wv / 4 for SwiGLU)
-    const int wmat = NMAT == 2 ? (wv >> 2) : 0;
-    const uint8_t* w_base = p.w_packed[wmat] + T.e * mat_codes;
-    uint32_t w_off[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = (wv * 2 + j) * 16 + (lane >> 2);
-      const int chunk = (lane & 3) ^ swz_w_key(n);
-      w_off[j] = (uint32_t)(T.nbase + pf_wrow<NMAT>(n)) * (uint32_t)(K / 2) + (uint32_t)chunk * 16u;
-    }
-    // scales: MX rows 64 (wv % 4) + lane (waves 4..7 write an unread copy); NV row 32 wv + lane / 2, half lane % 2
-    const int s_n = W_NV ? wv * 32 + (lane >> 1) : (wv & 3) * 64 + lane;
-    const int smat = NMAT == 2 ? (W_NV ? (wv >> 2) : ((wv >> 1) & 1)) : 0;
-    const uint8_t* s_base = p.w_scale[smat] + T.e * mat_scales;
-    const uint32_t s_off = (uint32_t)(T.nbase + pf_wrow<NMAT>(s_n)) * sc_row + (W_NV ? (lane & 1) * 4 : 0);
-
-    // load q (0..6) of step kb into stage S: 4 token loads, 2 weight-code loads, 1 scale load
-    auto issue_one = [&](auto S_tag, int kb, int q) {
-      uint8_t* st = pf_stage<decltype(S_tag)::value>();
-      if (q < 4) {
-        __builtin_amdgcn_global_load_lds((const void*)(p.a_data + kb * 256 + a_off[q]), (lds_void_t*)(st + (wv * 4 + q) * 1024),
-                                         16, 0, 0);
-      } else if (q < 6) {
-        const int j = q - 4;
-        __builtin_amdgcn_global_load_lds((const void*)(w_base + kb * 64 + w_off[j]),
-                                         (lds_void_t*)(st + kPfAStage + (wv * 2 + j) * 1024), 16, 0, 0);
-      } else {
-        __builtin_amdgcn_global_load_lds((const void*)(s_base + kb * (W_NV ? 8 : 4) + s_off),
-                                         (lds_void_t*)(st + kPfAStage + kPfWStage + wv * 256), 4, 0, 0);
-      }
-    };
-    auto issue = [&](auto S_tag, int kb) {
-#pragma unroll
-      for (int q = 0; q < kDmaPerStep; ++q) issue_one(S_tag, kb, q);
-    };
-
-    f32x4 acc[4][4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // step k from stage S: wait for this wave's loads of step k (those of step
-    // k + 1 may stay in flight), barrier (every wave's loads landed, every wave
-    // done with step k - 1), refill the stage of step k - 1 with step k + 2
-    // (past the end: step nk - 1 again, unread), compute
-    auto step = [&](auto S_tag, int k) {
-      constexpr int S = decltype(S_tag)::value;
-      __builtin_amdgcn_s_waitcnt((kDmaPerStep & 15) | (7 << 4) | (15 << 8));      // vmcnt(7)
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      const int kn = min(k + 2, nk - 1);
-      constexpr auto SN = std::integral_constant<int, (S + 2) % 3>();
-      // the next stage's loads go out between this step's MFMA slots (two per
-      // slot), so the load unit drains them while the matrix cores work
-      auto hook = [&](int s) {
-        issue_one(SN, kn, 2 * s);
-        if (2 * s + 1 < kDmaPerStep) issue_one(SN, kn, 2 * s + 1);
-      };
-      if (active) {
-        pf_compute<NMAT, WF>(pf_stage<S>(), acc, wm, wn, li, lg, hook);
-      } else {
-        issue(SN, kn);
-      }
-    };
-
-    __syncthreads();                                                 // previous tile done with the stages
-    issue(std::integral_constant<int, 0>(), 0);
-    issue(std::integral_constant<int, 1>(), min(1, nk - 1));
-    int kb = 0;
-    for (; kb + 3 <= nk; kb += 3) {
-      step(std::integral_constant<int, 0>(), kb);
-      step(std::integral_constant<int, 1>(), kb + 1);
-      step(std::integral_constant<int, 2>(), kb + 2);
-    }
-    if (kb < nk) step(std::integral_constant<int, 0>(), kb);
-    if (kb + 1 < nk) step(std::integral_constant<int, 1>(), kb + 1);
-
-    pf_epilogue<NMAT>(p, T, acc, wglob, wm, wn, li, lg);
-  }
-}
-
-// --------------------------------------- NVFP4 tokens: through registers
-// registers of one step in flight (per thread)
-struct PfRegs {
-  u32x4 a;                 // 32 token codes
-  uint32_t asc;            // their two E4M3 scales
-  u32x4 w[2];              // 2 weight-code chunks
-  uint32_t s;              // one dword of weight scales
-};
-
-template <int NMAT, int WF>
-__global__ __launch_bounds__(kPfThreads) void gemm_prefill_nv_kernel(GemmArgs p) {
-  constexpr bool W_NV = WF != 0;
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];      // 2 stages
-  __shared__ int s_pref[kPfMaxE + 1];
-  __shared__ int s_wc[kPfThreads / kWave];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wv = tid >> 6;
-  const int wm = wv >> 2, wn = wv & 3;                               // SIMD s holds waves s (wm 0) and s + 4 (wm 1)
-  const int li = lane & 15, lg = lane >> 4;
-  const int K = p.K, N = p.N;
-  const int ntn = N / (kPfBN / NMAT);
-  const int nk = K / kPfBK;                                          // even (checked on the host)
-  const int total = build_tile_table<kPfThreads>(p, ntn, s_pref, s_wc);
-  int t_begin, t_end, t_stride;
-  xcd_slice(total, t_begin, t_end, t_stride);
-
-  const uint32_t sc_row = (uint32_t)(W_NV ? K / 16 : K / 32);
-  const uint32_t mat_codes = (uint32_t)N * (uint32_t)(K / 2);
-  const uint32_t mat_scales = (uint32_t)N * sc_row;
-  const rsrc_t ar = make_rsrc(p.a_data, (uint32_t)p.a_bytes);
-  const rsrc_t asr = make_rsrc(p.a_scales, (uint32_t)(p.a_bytes / 8));
-  // the matrix of a load is uniform per wave: code chunk j of any thread is in
-  // matrix j (SwiGLU), a scale dword of wave w in matrix w / 4 (NV) or (w / 2) % 2 (MX)
-  const int wvu = __builtin_amdgcn_readfirstlane(wv);
-  const int smat = NMAT == 2 ? (W_NV ? (wvu >> 2) : ((wvu >> 1) & 1)) : 0;
-
-  for (int tile = t_begin; tile < t_end; tile += t_stride) {
-    const PfTile T = locate_tile<NMAT>(p, s_pref, tile);
-    const bool active = wm * 64 < T.mrows;                           // as in the bf16 kernel
-    rsrc_t wr[NMAT], sr[NMAT];
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m) {
-      wr[m] = make_rsrc(p.w_packed[m] + (int64_t)T.e * mat_codes, mat_codes);
-      sr[m] = make_rsrc(p.w_scale[m] + (int64_t)T.e * mat_scales, mat_scales);
-    }
-    const rsrc_t s_rsrc = smat == 0 ? sr[0] : sr[NMAT - 1];
-    float wglob[NMAT];
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m) wglob[m] = W_NV ? p.w_global[m][T.e] : 1.0f;
-
-    // tokens: row tid / 4, 32 codes (tid % 4) and their two scales
-    uint32_t a_off, as_off;
-    {
-      const int row = tid >> 2;
-      const int64_t r = T.rbase + min(row, T.mrows - 1);            // rows past the tile's end reread a valid row
-      const int64_t src = p.gather ? (int64_t)(p.gather[r] / p.gather_div) : r;
-      a_off = (uint32_t)(src * (K / 2)) + (uint32_t)(tid & 3) * 16u;
-      as_off = (uint32_t)(src * (K / 16)) + (uint32_t)(tid & 3) * 2u;
-    }
-    // weight codes: chunks q = tid + 512 j (row q / 4, chunk q % 4); scales: MX row tid % 256, NV row tid / 2, half tid % 2
-    uint32_t w_off[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int q = tid + kPfThreads * j;
-      w_off[j] = (uint32_t)(T.nbase + pf_wrow<NMAT>(q >> 2)) * (uint32_t)(K / 2) + (uint32_t)(q & 3) * 16u;
-    }
-    const int s_n = W_NV ? (tid >> 1) : (tid & 255);
-    const uint32_t s_off = (uint32_t)(T.nbase + pf_wrow<NMAT>(s_n)) * sc_row + (W_NV ? (uint32_t)(tid & 1) * 4u : 0u);
-
-    auto fetch = [&](PfRegs& R, int kb) {
-      R.a = bload128(ar, a_off + (uint32_t)kb * 64u, 0);
-      R.asc = bload16(asr, as_off + (uint32_t)kb * 8u, 0);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) R.w[j] = bload128(wr[NMAT == 2 ? j : 0], w_off[j] + (uint32_t)kb * 64u, 0);
-      R.s = bload32(s_rsrc, s_off + (uint32_t)kb * (W_NV ? 8u : 4u), 0);
-    };
-    auto store = [&](const PfRegs& R, uint8_t* st) {
-      uint8_t* sa = st;
-      uint8_t* sw = st + kPfAStage;
-      uint8_t* ss = st + kPfAStage + kPfWStage;
-      const int row = tid >> 2, c = tid & 3;
-      const float s_lo = e4m3_to_f32(R.asc & 0xFF) * p.a_gscale, s_hi = e4m3_to_f32((R.asc >> 8) & 0xFF) * p.a_gscale;
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        *(u32x4*)(sa + swz_a(row, c * 4 + s)) = __builtin_bit_cast(u32x4, fp4x8_to_bf16(R.a[s], s < 2 ? s_lo : s_hi));
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int q = tid + kPfThreads * j;
-        *(u32x4*)(sw + swz_w(q >> 2, q & 3)) = R.w[j];
-      }
-      // NV: row tid / 2, half tid % 2; MX: row tid (threads >= 256 write an unread copy)
-      *(uint32_t*)(ss + tid * 4) = R.s;
-    };
-
-    f32x4 acc[4][4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    uint8_t* st0 = lds;
-    uint8_t* st1 = lds + kPfStage;
-    PfRegs R0, R1;
-    __syncthreads();                                                 // previous tile done with LDS
-    fetch(R0, 0);
-    fetch(R1, 1);
-    store(R0, st0);
-    __syncthreads();
-    // Loads and stores are unconditional (past the last step they repeat it, from
-    // L2) so the compiler can count every wait exactly; scheduling fences keep
-    // each fetch at the top of its half-iteration.
-    for (int kb = 0; kb < nk; kb += 2) {
-      fetch(R0, min(kb + 2, nk - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      if (active) pf_compute<NMAT, WF>(st0, acc, wm, wn, li, lg);
-      __builtin_amdgcn_sched_barrier(0);
-      store(R1, st1);                                                // step kb + 1
-      __syncthreads();
-      fetch(R1, min(kb + 3, nk - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      if (active) pf_compute<NMAT, WF>(st1, acc, wm, wn, li, lg);
-      __builtin_amdgcn_sched_barrier(0);
-      store(R0, st0);                                                // step kb + 2
-      __syncthreads();
-    }
-
-    pf_epilogue<NMAT>(p, T, acc, wglob, wm, wn, li, lg);
-  }
-}
-
-// ------------------------------------------------------------------- host
-static int device_cus() {
-  static int cus = 0;
-  if (!cus) {
-    int dev = 0;
-    hipGetDevice(&dev);
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  }
-  return cus;
-}
-
-template <int NMAT, int WF, bool A_NV>
-static void launch_prefill_one(const GemmArgs& a, hipStream_t stream) {
-  // persistent: one workgroup per CU (8 waves); tiles are distributed on the device
-  if (A_NV) {
-    auto kern = gemm_prefill_nv_kernel<NMAT, WF>;
-    static bool attr_set = false;
-    if (!attr_set) {
-      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kPfStage);
-      attr_set = true;
-    }
-    hipLaunchKernelGGL(kern, dim3(device_cus()), dim3(kPfThreads), 2 * kPfStage, stream, a);
-  } else {
-    hipLaunchKernelGGL((gemm_prefill_dma_kernel<NMAT, WF>), dim3(device_cus()), dim3(kPfThreads), 0, stream, a);
-  }
-}
-
-template <int NMAT>
-static void launch_prefill_f(const GemmArgs& a, int wf, bool a_nv, hipStream_t stream) {
-  switch (wf) {
-    case 0: a_nv ? launch_prefill_one<NMAT, 0, true>(a, stream) : launch_prefill_one<NMAT, 0, false>(a, stream); break;
-    case 1: a_nv ? launch_prefill_one<NMAT, 1, true>(a, stream) : launch_prefill_one<NMAT, 1, false>(a, stream); break;
-    default: a_nv ? launch_prefill_one<NMAT, 2, true>(a, stream) : launch_prefill_one<NMAT, 2, false>(a, stream); break;
-  }
-}
-
-moe_status launch_gemm_decode(const GemmArgs&, bool swiglu, int wf, bool a_nv, int64_t rows, hipStream_t);
+moe_status launch_gemm_decode(const GemmArgs&, bool swiglu, int wf, bool a_nv, int64_t rows, int persistent, hipStream_t);
 
 moe_status launch_gemm_prefill(const GemmArgs& a, bool swiglu, int wf, bool a_nv, int64_t rows, hipStream_t stream) {
   const int bn = swiglu ? kPfBN / 2 : kPfBN;
   if (a.N % bn != 0 || a.K % (2 * kPfBK) != 0 || a.E > kPfMaxE) {
     // shapes the tiled kernels do not cover run on the weight-streaming kernel
-    return launch_gemm_decode(a, swiglu, wf, a_nv, rows, stream);
+    return launch_gemm_decode(a, swiglu, wf, a_nv, rows, 0, stream);
   }
-  if (swiglu) launch_prefill_f<2>(a, wf, a_nv, stream);
-  else launch_prefill_f<1>(a, wf, a_nv, stream);
+  a.tiled ? prefill_run<true>(a, swiglu, wf, a_nv, stream) : prefill_run<false>(a, swiglu, wf, a_nv, stream);
   return launch_status("moe_fp4_grouped_gemm(prefill)");
 }
 

@@ -118,6 +118,11 @@ typedef enum { MOE_FP4_MX = 0, MOE_FP4_NV = 1 } moe_fp4_format;
                                  scale applied by the convert instruction itself.  Setting it
                                  for other scales gives wrong results; leaving it clear is
                                  always correct (conversion through float). */
+#define MOE_FP4_TILED 2       /* codes and scales are in the tiled layout that
+                                 moe_fp4_tile_weights writes (needs n % 16 == 0 and
+                                 k % 512 == 0); same values, bit-identical results, and
+                                 every weight load of the kernels reads one contiguous
+                                 block */
 
 typedef struct {
   moe_fp4_format format;
@@ -127,8 +132,27 @@ typedef struct {
   const uint8_t* packed;      /* codes [E, n, k/2] ("weight_packed")                    */
   const uint8_t* scale;       /* MX: E8M0 [E, n, k/32] | NV: E4M3 [E, n, k/16]          */
   const float* global_scale;  /* NV: float [E] (per expert matrix) | MX: NULL            */
-  int32_t flags;              /* MOE_FP4_SCALES_POW2 or 0 (ignored for MX)              */
+  int32_t flags;              /* MOE_FP4_SCALES_POW2 (NV only) | MOE_FP4_TILED, or 0     */
 } moe_fp4_weights;
+
+/* Rearrange expert weights into the tiled layout (flag MOE_FP4_TILED): the
+ * values stay those of the model's MXFP4 / NVFP4 tensors, only their order in
+ * memory changes, so that a wavefront of the GEMM kernels reads each operand
+ * block as one contiguous run instead of 16 strided row pieces.  Per expert
+ * matrix [n, k] (tile t = rows 16t .. 16t+15):
+ *   codes:  column step s (k 128s .. 128s+127) of tile t is a 1024-byte block
+ *           at (t * (k/128) + s) * 1024; its byte 16*(16*c + r) + b is byte
+ *           64*s + 16*c + b of row 16t + r   (c < 4, r < 16, b < 16)
+ *   scales: column window w (k 512w .. 512w+511) of tile t is a block of
+ *           16*G bytes at (t * (k/512) + w) * 16*G; row 16t + r's G scale
+ *           bytes of the window sit at G*r   (MX: G = 16 E8M0; NV: G = 32 E4M3)
+ * Global scales are unchanged.  Needs n % 16 == 0 and k % 512 == 0; the
+ * outputs have the sizes of the inputs, must not overlap them and must be
+ * 16-byte aligned.  num_experts == 0 is a no-op.
+ */
+moe_status moe_fp4_tile_weights(moe_fp4_format format, int32_t num_experts, int32_t n, int32_t k,
+                                const uint8_t* packed, const uint8_t* scale, uint8_t* packed_tiled,
+                                uint8_t* scale_tiled, hipStream_t stream);
 
 typedef enum { MOE_ACT_BF16 = 0 /* W4A16 */, MOE_ACT_NVFP4 = 1 /* W4A4 */ } moe_act_mode;
 
@@ -156,8 +180,12 @@ typedef struct {
 } moe_out;
 
 #define MOE_ALGO_AUTO 0       /* choose by rows per expert                                */
-#define MOE_ALGO_DECODE 1     /* weight-streaming kernel (few rows per expert)            */
+#define MOE_ALGO_DECODE 1     /* weight-streaming kernel (few rows per expert): one
+                                 workgroup per (expert, block of output features)         */
 #define MOE_ALGO_PREFILL 2    /* LDS-tiled MFMA kernel (many rows per expert)             */
+#define MOE_ALGO_DECODE_PERSISTENT 3  /* weight streaming by persistent workgroups that walk
+                                 one work list (k 4096 or 2048, n >= 128; other shapes
+                                 run as MOE_ALGO_DECODE)                                  */
 
 moe_status moe_fp4_grouped_gemm(const moe_act* a, const moe_fp4_weights* w0, const moe_fp4_weights* w1,
                                 moe_epilogue epi, const int32_t* expert_offsets, int64_t rows,

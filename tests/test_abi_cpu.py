@@ -100,3 +100,26 @@ def test_combine_transcode_quant_reject():
 def test_status_strings():
     for s in range(5):
         assert moe.lib.moe_status_string(s)
+
+
+def test_tile_weights_rejects_bad_arguments():
+    t = moe.lib.moe_fp4_tile_weights
+    A, B, C, D = (ctypes.c_void_p(0x100000 * i) for i in (1, 2, 3, 4))
+    _err(t(moe.MOE_FP4_MX, 2, 250, 512, A, B, C, D, None), moe.MOE_ERR_INVALID)     # n % 16
+    _err(t(moe.MOE_FP4_MX, 2, 256, 640, A, B, C, D, None), moe.MOE_ERR_INVALID)     # k % 512
+    _err(t(7, 2, 256, 512, A, B, C, D, None), moe.MOE_ERR_INVALID)                  # format
+    _err(t(moe.MOE_FP4_MX, 2, 256, 512, A, B, None, D, None), moe.MOE_ERR_INVALID)  # NULL
+    _err(t(moe.MOE_FP4_MX, 2, 256, 512, A, B, A, D, None), moe.MOE_ERR_INVALID)     # in place
+    # codes [2, 256, 256] = 128 KiB from 0x100000: an output starting inside them overlaps
+    _err(t(moe.MOE_FP4_MX, 2, 256, 512, A, B, ctypes.c_void_p(0x100000 + 0x10000), D, None), moe.MOE_ERR_INVALID)
+    assert t(moe.MOE_FP4_MX, 0, 256, 512, None, None, None, None, None) == moe.MOE_OK   # no experts: no-op
+
+
+def test_gemm_checks_the_tiled_layout():
+    act = moe.Act(moe.MOE_ACT_BF16, 0x40000, None, 1.0, None, 1, 8)
+    w = moe.Fp4Weights(moe.MOE_FP4_MX, 4, 256, 640, 0x10000, 0x20000, None, moe.MOE_FP4_TILED)
+    _err(_gemm(act, w, w), moe.MOE_ERR_INVALID)                                  # tiled needs k % 512
+    w0 = moe.Fp4Weights(moe.MOE_FP4_MX, 4, 256, 512, 0x10000, 0x20000, None, moe.MOE_FP4_TILED)
+    w1 = moe.Fp4Weights(moe.MOE_FP4_MX, 4, 256, 512, 0x10000, 0x20000, None, 0)
+    _err(_gemm(act, w0, w1), moe.MOE_ERR_INVALID)                                # w0 / w1 layouts differ
+    _err(_gemm(act, w0, w0, algo=4), moe.MOE_ERR_INVALID)                        # bad algo

@@ -385,3 +385,118 @@ def test_grouped_gemm_model_k(algo, fmt, amode):
     zref = bf16_to_f64(oracle.round_to_bf16_bits(zref))
     assert_close_rms(bf16_to_f64(host_bf16_bits(z)), zref, what="z", ulp_rel=BF16_ULP)
     assert_close_rms(bf16_to_f64(host_bf16_bits(o)), oref, what="o", ulp_rel=BF16_ULP)
+
+
+PERSIST_COUNTS = [0, 1, 17, 150, 400, 33, 0, 64]      # 8-row passes: 0+1+3+19+50+5+0+8 segments
+
+
+@pytest.mark.parametrize("fmt,general,amode", [("mx", False, "bf16"), ("nv", False, "bf16"), ("nv", True, "nvfp4"),
+                                               ("mx", False, "nvfp4")])
+def test_grouped_gemm_persistent_parity(fmt, general, amode):
+    """The persistent weight-streaming kernel at the model's K, forced on a ragged batch:
+    experts of many 8-row passes, work slices that cross segment boundaries, several
+    rounds of 8 units per workgroup (gate/up: 64 units per segment)."""
+    E, H, I, D = 8, 4096, 1024, 256
+    counts = np.array(PERSIST_COUNTS)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offsets[-1])
+    tsrc = 300
+    say(f"gemm persistent fmt={fmt} general={general} amode={amode} R={R}")
+    x = synth.random_bf16(81, (tsrc, H))
+    gather = np.random.default_rng(82).integers(0, tsrc * 8, size=R).astype(np.int32)
+    wg, dg = _gemm_problem(83, E, I, H, counts, tsrc, fmt, general)
+    wu, du = _gemm_problem(84, E, I, H, counts, tsrc, fmt, general)
+    wd, dd = _gemm_problem(85, E, D, 2048, counts, R, fmt, general)
+    if amode == "nvfp4":
+        xc, xs = oracle.quantize_nvfp4(x, 1.0)
+        a_val, a_dev, a_sc = oracle.dequant_nvfp4_act(xc, xs), dev_u8(xc), dev_u8(xs)
+    else:
+        a_val, a_dev, a_sc = bf16_to_f64(x), dev_bf16(x), None
+    algo = moe.MOE_ALGO_DECODE_PERSISTENT
+    zc = torch.empty((R, I // 2), dtype=torch.uint8, device="cuda")
+    zs = torch.empty((R, I // 16), dtype=torch.uint8, device="cuda")
+    z = moe.grouped_gemm(a_dev, wg, wu, dev_i32(offsets), R, gather=dev_i32(gather), gather_div=8, a_scales=a_sc,
+                         out_codes=zc, out_scales=zs, algo=algo)
+    z_again = moe.grouped_gemm(a_dev, wg, wu, dev_i32(offsets), R, gather=dev_i32(gather), gather_div=8,
+                               a_scales=a_sc, algo=algo)
+    z2 = synth.random_bf16(86, (R, 2048))
+    o = moe.grouped_gemm(dev_bf16(z2), wd, None, dev_i32(offsets), R, algo=algo)
+    torch.cuda.synchronize()
+    zb = host_bf16_bits(z)
+    assert np.array_equal(zb, host_bf16_bits(z_again)), "not deterministic"
+    zref = np.zeros((R, I))
+    oref = np.zeros((R, D))
+    z2v = bf16_to_f64(z2)
+    for e in range(E):
+        rows = slice(offsets[e], offsets[e + 1])
+        a = a_val[gather[rows] // 8]
+        zref[rows] = oracle.silu(a @ dg[e].T) * (a @ du[e].T)
+        oref[rows] = z2v[rows] @ dd[e].T
+    zref = bf16_to_f64(oracle.round_to_bf16_bits(zref))
+    assert_close_rms(bf16_to_f64(zb), zref, what="z", ulp_rel=BF16_ULP)
+    assert_close_rms(bf16_to_f64(host_bf16_bits(o)), oref, what="o", ulp_rel=BF16_ULP)
+    c_ref, s_ref = oracle.quantize_nvfp4(zb, 1.0)
+    assert np.array_equal(host(zs), s_ref)
+    assert np.array_equal(host(zc), c_ref)
+
+
+def _tile_ref(codes, scales, nv):
+    """The tiled layout as the C header defines it, by reshaping (numpy)."""
+    E, n, kb = codes.shape
+    k = 2 * kb
+    c = codes.reshape(E, n // 16, 16, k // 128, 4, 16)              # e, t, r, s, c, b
+    c = c.transpose(0, 1, 3, 4, 2, 5).reshape(E, n, kb)             # e, t, s, c, r, b
+    G = 32 if nv else 16
+    sc = scales.reshape(E, n // 16, 16, k // 512, G)                # e, t, r, w, g
+    sc = sc.transpose(0, 1, 3, 2, 4).reshape(scales.shape)          # e, t, w, r, g
+    return np.ascontiguousarray(c), np.ascontiguousarray(sc)
+
+
+@pytest.mark.parametrize("nv", [False, True])
+def test_tile_weights_layout(nv):
+    E, n, k = 3, 48, 1536
+    say(f"tile weights nv={nv} E={E} n={n} k={k}")
+    rng = np.random.default_rng(91)
+    codes = rng.integers(0, 256, size=(E, n, k // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, size=(E, n, k // (16 if nv else 32)), dtype=np.uint8)
+    g = dev_f32(np.ones(E, np.float32)) if nv else None
+    w = moe.tile_weights(moe.Weights(dev_u8(codes), dev_u8(scales), g))
+    torch.cuda.synchronize()
+    c_ref, s_ref = _tile_ref(codes, scales, nv)
+    assert w.tiled
+    assert np.array_equal(host(w.packed), c_ref)
+    assert np.array_equal(host(w.scale), s_ref)
+
+
+@pytest.mark.parametrize("algo", [moe.MOE_ALGO_DECODE, moe.MOE_ALGO_DECODE_PERSISTENT, moe.MOE_ALGO_PREFILL])
+@pytest.mark.parametrize("fmt,general,amode", [("mx", False, "bf16"), ("nv", False, "bf16"), ("nv", True, "nvfp4"),
+                                               ("mx", False, "nvfp4")])
+def test_grouped_gemm_tiled_is_bitwise_row_major(algo, fmt, general, amode):
+    """Same values in another order: the tiled layout gives bit-identical outputs
+    (SwiGLU at K 4096 and down at K 2048, ragged experts with many 8-row passes)."""
+    E, H, I, D = 8, 4096, 512, 256
+    counts = np.array(PERSIST_COUNTS)
+    offsets = dev_i32(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32))
+    R = int(counts.sum())
+    tsrc = 300
+    say(f"gemm tiled algo={algo} fmt={fmt} general={general} amode={amode} R={R}")
+    x = synth.random_bf16(92, (tsrc, H))
+    gather = dev_i32(np.random.default_rng(93).integers(0, tsrc * 8, size=R).astype(np.int32))
+    wg, _ = _gemm_problem(94, E, I, H, counts, tsrc, fmt, general)
+    wu, _ = _gemm_problem(95, E, I, H, counts, tsrc, fmt, general)
+    wd, _ = _gemm_problem(96, E, D, 2048, counts, R, fmt, general)
+    if amode == "nvfp4":
+        xc, xs = oracle.quantize_nvfp4(x, 1.0)
+        a_dev, a_sc = dev_u8(xc), dev_u8(xs)
+    else:
+        a_dev, a_sc = dev_bf16(x), None
+    z2 = dev_bf16(synth.random_bf16(97, (R, 2048)))
+    outs = []
+    for tiled in (False, True):
+        g, u, d = (moe.tile_weights(w) if tiled else w for w in (wg, wu, wd))
+        z = moe.grouped_gemm(a_dev, g, u, offsets, R, gather=gather, gather_div=8, a_scales=a_sc, algo=algo)
+        o = moe.grouped_gemm(z2, d, None, offsets, R, algo=algo)
+        torch.cuda.synchronize()
+        outs.append((host_bf16_bits(z), host_bf16_bits(o)))
+    assert np.array_equal(outs[0][0], outs[1][0]), "gate/up differs between layouts"
+    assert np.array_equal(outs[0][1], outs[1][1]), "down differs between layouts"

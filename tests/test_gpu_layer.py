@@ -175,6 +175,26 @@ def test_decode_layer_hip_graph(decode_weights, T):
         assert np.array_equal(host_bf16_bits(y_static), y_ref), f"replay {rep} differs from eager"
 
 
+def tiled(dw):
+    return moe.LayerWeights(*(moe.tile_weights(getattr(dw, n)) for n in ("gate", "up", "down")))
+
+
+@pytest.mark.parametrize("T", [8, 64])
+def test_decode_layer_tiled(decode_weights, T):
+    """The decode layer on weights in the tiled layout: the oracle's routing,
+    permutation and tolerances, and the same bytes as on row-major weights."""
+    W, dw, cache = decode_weights
+    yb, _ = check_layer(synth.WORKLOADS["decode"], T, W, "mx", "bf16", [0, T - 1], dev_weights=tiled(dw),
+                        cache=cache)
+    w = synth.WORKLOADS["decode"]
+    s = w.shape
+    layer = moe.MoELayer(dw, s.num_experts, s.n_group, s.topk_group, s.top_k, s.routed_scaling_factor, T)
+    y = layer.forward(dev_bf16(synth.activations(w, T)), dev_f32(synth.logits(w, T)),
+                      dev_f32(synth.correction_bias(w)) if synth.correction_bias(w) is not None else None)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bf16_bits(y), yb)
+
+
 def test_decode_mx_equals_nv_bitwise(decode_weights):
     """W4A16 on MX weights and on their NV transcode give identical bytes."""
     W, dw, _ = decode_weights
@@ -203,7 +223,9 @@ def test_decode_mx_equals_nv_bitwise(decode_weights):
 def test_prefill_layer():
     w = synth.WORKLOADS["prefill"]
     W = synth.expert_weights(w)
-    check_layer(w, 8192, W, "mx", "bf16", [0, 4097, 8191])
+    yb, cache = check_layer(w, 8192, W, "mx", "bf16", [0, 4097, 8191])
+    # the same layer on tiled weights: the oracle's tolerances (sampled tokens)
+    check_layer(w, 8192, W, "mx", "bf16", [1, 8190], dev_weights=tiled(upload_weights(W, "mx")), cache=cache)
 
 
 def test_w4a4_layer():
