@@ -12,8 +12,8 @@
 //     convert instruction and runs 4 x 4 bf16 16x16x32 MFMA tiles (64 tokens
 //     x 64 weight rows); the token operands of the next k-slot are read while
 //     the current slot's MFMAs run;
-//   * LDS layouts are XOR-swizzled so the MFMA operand reads are conflict
-//     free: token chunk c (16 B) of row r at c ^ (r % 16) in a 256-B row,
+//   * LDS layouts are swizzled so the MFMA operand reads are conflict
+//     free: token chunk c (16 B) of row r at a linear map of (c, r) in a 256-B row,
 //     weight chunk c of row n at c ^ ((n / 2 ^ n / 8) % 4) in a 64-B row;
 //   * persistent workgroups: the tile list, ordered (expert, n-tile, m-tile),
 //     is cut into one contiguous slice per XCD (workgroup b runs on XCD b % 8),
@@ -51,7 +51,22 @@ __shared__ __attribute__((aligned(16))) uint8_t pf_stage2[kPfStage];
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-__device__ __forceinline__ uint32_t swz_a(int row, int chunk) { return (uint32_t)(row * 256 + ((chunk ^ (row & 15)) << 4)); }
+// Token stage: 16-byte chunk c of row r sits at slot P(c) ^ f(r) of the row's
+// 256 bytes, P swapping bits 2 and 3 of c, f(r) = r % 4 + 4 * (r / 8 % 2).
+// gfx950 serves a ds_read_b128 in lane groups for which the plain c ^ (r % 16)
+// puts two lanes on the same banks (measured: half the LDS cycles were
+// conflicts); this linear map keeps the 16 lanes of every group on distinct
+// banks for each k-slot of the MFMA operand read.
+__device__ __forceinline__ int swz_a_slot(int row, int chunk) {
+  const int p = (chunk & 3) | ((chunk >> 3) & 1) << 2 | ((chunk >> 2) & 1) << 3;
+  return p ^ ((row & 3) | ((row >> 3) & 1) << 2);
+}
+// the chunk stored at slot `slot` of row `row` (the inverse map: P is its own inverse)
+__device__ __forceinline__ int swz_a_chunk(int row, int slot) {
+  const int q = slot ^ ((row & 3) | ((row >> 3) & 1) << 2);
+  return (q & 3) | ((q >> 3) & 1) << 2 | ((q >> 2) & 1) << 3;
+}
+__device__ __forceinline__ uint32_t swz_a(int row, int chunk) { return (uint32_t)(row * 256 + (swz_a_slot(row, chunk) << 4)); }
 // (n / 2 ^ n / 8) % 4 keeps any 8 consecutive rows (one 128-B bank sweep) and
 // any 16 consecutive rows (one 256-B sweep) on distinct 16-B slots
 __device__ __forceinline__ int swz_w_key(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
@@ -315,7 +330,7 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_dma_kernel(GemmArgs p
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = (wv * 4 + i) * 4 + (lane >> 4);
-      const int chunk = (lane & 15) ^ (row & 15);
+      const int chunk = swz_a_chunk(row, lane & 15);
       const int64_t r = T.rbase + min(row, T.mrows - 1);            // rows past the tile's end reread a valid row
       const int64_t src = p.gather ? (int64_t)(p.gather[r] / p.gather_div) : r;
       a_off[i] = (uint32_t)(src * (int64_t)K * 2) + (uint32_t)chunk * 16u;   // < 2 GiB (checked on the host)
