@@ -5,9 +5,10 @@
 // "MiMo-V2.6-Flash -- REAP-50", "Pruning Method"; MXFP4 / NVFP4 weights with
 // FP32 accumulation, "AxionML / MiMo-V2.6-Flash-MOPD-NVFP4", "About NVFP4
 // quantization"), tiled for reuse:
-//   * a workgroup of 8 waves owns a tile of BM = 128 token rows x BN = 256
-//     weight rows (SwiGLU: 128 gate + 128 up rows of the same outputs) and
-//     walks K in steps of BK = 128;
+//   * a workgroup of 8 waves owns a tile of BM token rows x BN weight rows
+//     (SwiGLU: BN/2 gate + BN/2 up rows of the same outputs) and walks K in
+//     steps of BK = 128; bf16 tokens use 64 x 512 tiles (one wave along
+//     tokens, eight along weight rows) where N allows, else 128 x 256 (2 x 4);
 //   * each wave dequantises its 64 weight rows from LDS with the gfx950
 //     convert instruction and runs 4 x 4 bf16 16x16x32 MFMA tiles (64 tokens
 //     x 64 weight rows); the token operands of the next k-slot are read while
@@ -34,20 +35,34 @@
 
 namespace moe {
 
-constexpr int kPfBM = 128, kPfBN = 256, kPfBK = 128;
-constexpr int kPfThreads = 512;                          // 8 waves: 2 along tokens x 4 along weight rows
-constexpr int kPfAStage = kPfBM * kPfBK * 2;             // 32 KB of bf16 tokens
-constexpr int kPfWStage = kPfBN * kPfBK / 2;             // 16 KB of FP4 codes
-constexpr int kPfSStage = kPfBN * 8;                     // 2 KB of scales (MX uses 4 B per row)
-constexpr int kPfStage = kPfAStage + kPfWStage + kPfSStage;
-constexpr int kPfMaxE = 1024;
+constexpr int kPfBK = 128;
+constexpr int kPfThreads = 512;                          // 8 waves of 64 tokens x 64 weight rows each
+constexpr int kPfMaxE = 1000;                            // tile prefix table in LDS beside three stages
 constexpr int kPfXcds = 8;
+
+// Tile shapes: BM token rows x BN weight rows (SwiGLU: BN/2 gate + BN/2 up rows
+// of the same outputs), BM/64 waves along tokens x WN along weight rows.
+template <int BM_, int BN_>
+struct PfShape {
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int WN = 8 / (BM / 64);
+  static constexpr int AStage = BM * kPfBK * 2;            // bf16 tokens
+  static constexpr int WStage = BN * kPfBK / 2;            // FP4 codes
+  static constexpr int SStage = BN * 8;                    // scales (MX uses half)
+  static constexpr int Stage = AStage + WStage + SStage;
+};
+// 128 x 256: the NVFP4-token kernel, and N not a multiple of 512 (256 SwiGLU)
+using PfTall = PfShape<128, 256>;
+// 64 x 512: bf16 tokens; pads experts in 64-row units, reads each token row
+// for half as many n-tiles, and dequantises each weight row in one wave only
+using PfWide = PfShape<64, 512>;
+constexpr int kPfStageMax = PfWide::Stage > PfTall::Stage ? PfWide::Stage : PfTall::Stage;
 
 // the three stages of the direct-to-LDS pipeline: separate objects, so the
 // compiler can tell a stage being read from the stages being filled
-__shared__ __attribute__((aligned(16))) uint8_t pf_stage0[kPfStage];
-__shared__ __attribute__((aligned(16))) uint8_t pf_stage1[kPfStage];
-__shared__ __attribute__((aligned(16))) uint8_t pf_stage2[kPfStage];
+__shared__ __attribute__((aligned(16))) uint8_t pf_stage0[kPfStageMax];
+__shared__ __attribute__((aligned(16))) uint8_t pf_stage1[kPfStageMax];
+__shared__ __attribute__((aligned(16))) uint8_t pf_stage2[kPfStageMax];
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -93,7 +108,7 @@ __device__ __forceinline__ uint32_t quant4_lanes(const float* v, float inv_g, ui
 
 // ---------------------------------------------------------------- tiles
 // s_pref[e] = tiles before expert e (expert e owns ceil(rows_e / BM) * ntn tiles)
-template <int NTHR>
+template <int NTHR, int BM>
 __device__ __forceinline__ int build_tile_table(const GemmArgs& p, int ntn, int* s_pref, int* s_wc) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int running = 0;
@@ -103,7 +118,7 @@ __device__ __forceinline__ int build_tile_table(const GemmArgs& p, int ntn, int*
     if (e < p.E) {
       int r0 = (int)max((int64_t)0, min((int64_t)p.offsets[e], p.rows));
       int r1 = (int)max((int64_t)r0, min((int64_t)p.offsets[e + 1], p.rows));
-      cnt = ((r1 - r0 + kPfBM - 1) / kPfBM) * ntn;
+      cnt = ((r1 - r0 + BM - 1) / BM) * ntn;
     }
     int x = cnt;
 #pragma unroll
@@ -131,7 +146,7 @@ struct PfTile {
 };
 
 // (expert, n-tile, m-tile) of a tile index; the m-tiles of one n-tile are consecutive
-template <int NMAT>
+template <int NMAT, typename SH>
 __device__ __forceinline__ PfTile locate_tile(const GemmArgs& p, const int* s_pref, int tile) {
   int lo = 0, hi = p.E - 1;
   while (lo < hi) {
@@ -143,12 +158,12 @@ __device__ __forceinline__ PfTile locate_tile(const GemmArgs& p, const int* s_pr
   t.e = lo;
   const int r0 = (int)max((int64_t)0, min((int64_t)p.offsets[lo], p.rows));
   const int r1 = (int)max((int64_t)r0, min((int64_t)p.offsets[lo + 1], p.rows));
-  const int mt_cnt = (r1 - r0 + kPfBM - 1) / kPfBM;
+  const int mt_cnt = (r1 - r0 + SH::BM - 1) / SH::BM;
   const int local = tile - s_pref[lo];
   const int nt = local / mt_cnt, mt = local % mt_cnt;
-  t.rbase = r0 + mt * kPfBM;
-  t.mrows = min(kPfBM, r1 - t.rbase);
-  t.nbase = nt * (kPfBN / NMAT);                                    // first row of each matrix's slab
+  t.rbase = r0 + mt * SH::BM;
+  t.mrows = min(SH::BM, r1 - t.rbase);
+  t.nbase = nt * (SH::BN / NMAT);                                   // first row of each matrix's slab
   return t;
 }
 
@@ -161,13 +176,13 @@ __device__ __forceinline__ void xcd_slice(int total, int& begin, int& end, int& 
   end = (int)((int64_t)total * (xcd + 1) / nx);
 }
 
-// block-local weight row n (0..255): matrix n / 128 (SwiGLU), row within the slab
-template <int NMAT>
-__device__ __forceinline__ int pf_wrow(int n) { return NMAT == 2 ? (n & 127) : n; }
+// block-local weight row n (0..BN-1): matrix n / (BN/2) (SwiGLU), row within the slab
+template <int NMAT, int BN>
+__device__ __forceinline__ int pf_wrow(int n) { return NMAT == 2 ? (n & (BN / 2 - 1)) : n; }
 // wave (wm, wn)'s weight group g (16 rows): block-local row base
-template <int NMAT>
+template <int NMAT, int BN>
 __device__ __forceinline__ int pf_lrow(int wn, int g) {
-  return NMAT == 2 ? (g >> 1) * 128 + wn * 32 + (g & 1) * 16 : wn * 64 + g * 16;
+  return NMAT == 2 ? (g >> 1) * (BN / 2) + wn * 32 + (g & 1) * 16 : wn * 64 + g * 16;
 }
 
 // Scale bytes of global weight row R for one step: a per-lane part and a
@@ -200,18 +215,18 @@ struct PfNoHook {
 // of the next stage's loads there, between MFMAs).
 // TL: the weight stage holds each 16-row group as one 1 KB tiled block (lane
 // (li, lg) at 16 * (16 lg + li)) instead of swizzled rows.
-template <int NMAT, int WF, bool TL, typename Hook = PfNoHook>
+template <int NMAT, int WF, bool TL, typename SH, typename Hook = PfNoHook>
 __device__ __forceinline__ void pf_compute(const uint8_t* st, f32x4 (&acc)[4][4], int wm, int wn, int li, int lg,
                                            Hook&& hook = Hook()) {
   constexpr bool W_NV = WF != 0;
   const uint8_t* sa = st;
-  const uint8_t* sw = st + kPfAStage;
-  const uint8_t* ss = st + kPfAStage + kPfWStage;
+  const uint8_t* sw = st + SH::AStage;
+  const uint8_t* ss = st + SH::AStage + SH::WStage;
   u32x4 wq[4];
   float s_lo[4], s_hi[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    const int n = pf_lrow<NMAT>(wn, g) + li;
+    const int n = pf_lrow<NMAT, SH::BN>(wn, g) + li;
     wq[g] = *(const u32x4*)(sw + (TL ? (uint32_t)(n >> 4) * 1024u + (uint32_t)(lg * 16 + li) * 16u : swz_w(n, lg)));
     if (W_NV) {
       const uint32_t b2 = *(const uint16_t*)(ss + n * 8 + lg * 2);
@@ -291,22 +306,30 @@ __device__ __forceinline__ uint8_t* pf_stage() {
   return S == 0 ? pf_stage0 : (S == 1 ? pf_stage1 : pf_stage2);
 }
 
-template <int NMAT, int WF, bool TL>
+template <int NMAT, int WF, bool TL, typename SH>
 __global__ __launch_bounds__(kPfThreads) void gemm_prefill_dma_kernel(GemmArgs p) {
   constexpr bool W_NV = WF != 0;
+  static_assert(3 * SH::Stage + (kPfMaxE + 1) * 4 + kPfThreads / kWave * 4 <= 160 * 1024, "LDS");
   __shared__ int s_pref[kPfMaxE + 1];
   __shared__ int s_wc[kPfThreads / kWave];
-  constexpr int kDmaPerStep = 7;                                     // direct-to-LDS loads per wave and step
+  // direct-to-LDS loads per wave and step: tokens (1 KB = 4 rows each), weight
+  // codes (1 KB = 16 rows), scales (256 B: 64 MX rows or 32 NV rows)
+  constexpr int kA = SH::BM / 32, kW = SH::BN / 128;
+  constexpr int kSRows = W_NV ? 32 : 64;                              // weight rows per scale load
+  constexpr int kSLoads = SH::BN / kSRows;                            // scale loads per step (all waves)
+  constexpr int kS = kSLoads > 8 ? kSLoads / 8 : 1;                   // per wave (MX 128 x 256: waves 4..7 repeat 0..3)
+  constexpr int kDmaPerStep = kA + kW + kS;
+  static_assert(kDmaPerStep <= 8, "two loads per k-slot");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wv >> 2, wn = wv & 3;                               // SIMD s holds waves s (wm 0) and s + 4 (wm 1)
+  const int wm = wv / SH::WN, wn = wv % SH::WN;                      // (128 x 256: SIMD s holds waves s and s + 4)
   const int li = lane & 15, lg = lane >> 4;
   const int K = p.K, N = p.N;
-  const int ntn = N / (kPfBN / NMAT);
+  const int ntn = N / (SH::BN / NMAT);
   const int nk = K / kPfBK;
-  const int total = build_tile_table<kPfThreads>(p, ntn, s_pref, s_wc);
+  const int total = build_tile_table<kPfThreads, SH::BM>(p, ntn, s_pref, s_wc);
   int t_begin, t_end, t_stride;
   xcd_slice(total, t_begin, t_end, t_stride);
 
@@ -315,7 +338,7 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_dma_kernel(GemmArgs p
   const int64_t mat_scales = (int64_t)N * sc_row;
 
   for (int tile = t_begin; tile < t_end; tile += t_stride) {
-    const PfTile T = locate_tile<NMAT>(p, s_pref, tile);
+    const PfTile T = locate_tile<NMAT, SH>(p, s_pref, tile);
     // a wave whose 64 token rows all lie past the tile's end skips its MFMA
     // work (its SIMD then runs the other wave alone); it still loads and syncs
     const bool active = wm * 64 < T.mrows;
@@ -325,51 +348,59 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_dma_kernel(GemmArgs p
 
     // per-lane sources of this wave's loads as 32-bit offsets from uniform
     // bases (scalar registers); LDS slot = wave base + lane * size
-    // tokens: load i fills rows 4 * (4 wv + i) .. +3, lane -> (row, slot lane % 16)
-    uint32_t a_off[4];
+    // tokens: load i fills rows 4 * (kA wv + i) .. +3, lane -> (row, slot lane % 16)
+    uint32_t a_off[kA];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = (wv * 4 + i) * 4 + (lane >> 4);
+    for (int i = 0; i < kA; ++i) {
+      const int row = (wv * kA + i) * 4 + (lane >> 4);
       const int chunk = swz_a_chunk(row, lane & 15);
       const int64_t r = T.rbase + min(row, T.mrows - 1);            // rows past the tile's end reread a valid row
       const int64_t src = p.gather ? (int64_t)(p.gather[r] / p.gather_div) : r;
       a_off[i] = (uint32_t)(src * (int64_t)K * 2) + (uint32_t)chunk * 16u;   // < 2 GiB (checked on the host)
     }
-    // weight codes: load j fills rows 16 * (2 wv + j) .. +15 (matrix wv / 4 for SwiGLU);
+    // weight codes: load j fills rows 16 * (kW wv + j) .. +15 (matrix wv / 4 for SwiGLU);
     // tiled: that group's 1 KB block of the step, in lane order
     const int wmat = NMAT == 2 ? (wv >> 2) : 0;
     const uint8_t* w_base = p.w_packed[wmat] + T.e * mat_codes;
-    uint32_t w_off[2];
+    uint32_t w_off[kW];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < kW; ++j) {
       if (TL) {
-        const int tile = (T.nbase + pf_wrow<NMAT>((wv * 2 + j) * 16)) >> 4;
+        const int tile = (T.nbase + pf_wrow<NMAT, SH::BN>((wv * kW + j) * 16)) >> 4;
         w_off[j] = (uint32_t)tile * (uint32_t)(K / 128) * 1024u + (uint32_t)lane * 16u;
       } else {
-        const int n = (wv * 2 + j) * 16 + (lane >> 2);
+        const int n = (wv * kW + j) * 16 + (lane >> 2);
         const int chunk = (lane & 3) ^ swz_w_key(n);
-        w_off[j] = (uint32_t)(T.nbase + pf_wrow<NMAT>(n)) * (uint32_t)(K / 2) + (uint32_t)chunk * 16u;
+        w_off[j] = (uint32_t)(T.nbase + pf_wrow<NMAT, SH::BN>(n)) * (uint32_t)(K / 2) + (uint32_t)chunk * 16u;
       }
     }
-    // scales: MX rows 64 (wv % 4) + lane (waves 4..7 write an unread copy); NV row 32 wv + lane / 2, half lane % 2
-    const int s_n = W_NV ? wv * 32 + (lane >> 1) : (wv & 3) * 64 + lane;
-    const int smat = NMAT == 2 ? (W_NV ? (wv >> 2) : ((wv >> 1) & 1)) : 0;
-    const uint8_t* s_base = p.w_scale[smat] + T.e * mat_scales;
-    const uint32_t s_off = pf_scale_lane<TL, W_NV>(T.nbase + pf_wrow<NMAT>(s_n), lane & 1, K);
+    // scales: load h covers rows kSRows * ((kS wv + h) % kSLoads) ..; MX one row per
+    // lane, NV row lane / 2 with half lane % 2; LDS slot 256 * (kS wv + h)
+    const uint8_t* s_base[kS];
+    uint32_t s_off[kS];
+#pragma unroll
+    for (int h = 0; h < kS; ++h) {
+      const int ld = (wv * kS + h) % kSLoads;
+      const int s_n = ld * kSRows + (W_NV ? (lane >> 1) : lane);
+      const int smat = NMAT == 2 ? (ld * kSRows) / (SH::BN / 2) : 0;
+      s_base[h] = p.w_scale[smat] + T.e * mat_scales;
+      s_off[h] = pf_scale_lane<TL, W_NV>(T.nbase + pf_wrow<NMAT, SH::BN>(s_n), lane & 1, K);
+    }
 
-    // load q (0..6) of step kb into stage S: 4 token loads, 2 weight-code loads, 1 scale load
+    // load q of step kb into stage S: kA token loads, kW weight-code loads, kS scale loads
     auto issue_one = [&](auto S_tag, int kb, int q) {
       uint8_t* st = pf_stage<decltype(S_tag)::value>();
-      if (q < 4) {
-        __builtin_amdgcn_global_load_lds((const void*)(p.a_data + kb * 256 + a_off[q]), (lds_void_t*)(st + (wv * 4 + q) * 1024),
-                                         16, 0, 0);
-      } else if (q < 6) {
-        const int j = q - 4;
+      if (q < kA) {
+        __builtin_amdgcn_global_load_lds((const void*)(p.a_data + kb * 256 + a_off[q]),
+                                         (lds_void_t*)(st + (wv * kA + q) * 1024), 16, 0, 0);
+      } else if (q < kA + kW) {
+        const int j = q - kA;
         __builtin_amdgcn_global_load_lds((const void*)(w_base + kb * (TL ? 1024 : 64) + w_off[j]),
-                                         (lds_void_t*)(st + kPfAStage + (wv * 2 + j) * 1024), 16, 0, 0);
+                                         (lds_void_t*)(st + SH::AStage + (wv * kW + j) * 1024), 16, 0, 0);
       } else {
-        __builtin_amdgcn_global_load_lds((const void*)(s_base + pf_scale_step<TL, W_NV>(kb) + s_off),
-                                         (lds_void_t*)(st + kPfAStage + kPfWStage + wv * 256), 4, 0, 0);
+        const int h = q - kA - kW;
+        __builtin_amdgcn_global_load_lds((const void*)(s_base[h] + pf_scale_step<TL, W_NV>(kb) + s_off[h]),
+                                         (lds_void_t*)(st + SH::AStage + SH::WStage + (wv * kS + h) * 256), 4, 0, 0);
       }
     };
     auto issue = [&](auto S_tag, int kb) {
@@ -389,7 +420,7 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_dma_kernel(GemmArgs p
     // (past the end: step nk - 1 again, unread), compute
     auto step = [&](auto S_tag, int k) {
       constexpr int S = decltype(S_tag)::value;
-      __builtin_amdgcn_s_waitcnt((kDmaPerStep & 15) | (7 << 4) | (15 << 8));      // vmcnt(7)
+      __builtin_amdgcn_s_waitcnt((kDmaPerStep & 15) | (7 << 4) | (15 << 8));      // vmcnt(kDmaPerStep)
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
       const int kn = min(k + 2, nk - 1);
@@ -397,11 +428,11 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_dma_kernel(GemmArgs p
       // the next stage's loads go out between this step's MFMA slots (two per
       // slot), so the load unit drains them while the matrix cores work
       auto hook = [&](int s) {
-        issue_one(SN, kn, 2 * s);
+        if (2 * s < kDmaPerStep) issue_one(SN, kn, 2 * s);
         if (2 * s + 1 < kDmaPerStep) issue_one(SN, kn, 2 * s + 1);
       };
       if (active) {
-        pf_compute<NMAT, WF, TL>(pf_stage<S>(), acc, wm, wn, li, lg, hook);
+        pf_compute<NMAT, WF, TL, SH>(pf_stage<S>(), acc, wm, wn, li, lg, hook);
       } else {
         issue(SN, kn);
       }
@@ -444,9 +475,9 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_nv_kernel(GemmArgs p)
   const int wm = wv >> 2, wn = wv & 3;                               // SIMD s holds waves s (wm 0) and s + 4 (wm 1)
   const int li = lane & 15, lg = lane >> 4;
   const int K = p.K, N = p.N;
-  const int ntn = N / (kPfBN / NMAT);
+  const int ntn = N / (PfTall::BN / NMAT);
   const int nk = K / kPfBK;                                          // even (checked on the host)
-  const int total = build_tile_table<kPfThreads>(p, ntn, s_pref, s_wc);
+  const int total = build_tile_table<kPfThreads, PfTall::BM>(p, ntn, s_pref, s_wc);
   int t_begin, t_end, t_stride;
   xcd_slice(total, t_begin, t_end, t_stride);
 
@@ -461,7 +492,7 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_nv_kernel(GemmArgs p)
   const int smat = NMAT == 2 ? (W_NV ? (wvu >> 2) : ((wvu >> 1) & 1)) : 0;
 
   for (int tile = t_begin; tile < t_end; tile += t_stride) {
-    const PfTile T = locate_tile<NMAT>(p, s_pref, tile);
+    const PfTile T = locate_tile<NMAT, PfTall>(p, s_pref, tile);
     const bool active = wm * 64 < T.mrows;                           // as in the bf16 kernel
     rsrc_t wr[NMAT], sr[NMAT];
 #pragma unroll
@@ -490,14 +521,14 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_nv_kernel(GemmArgs p)
     for (int j = 0; j < 2; ++j) {
       const int q = tid + kPfThreads * j;
       if (TL) {
-        const int tile = (T.nbase + pf_wrow<NMAT>((q >> 6) * 16)) >> 4;
+        const int tile = (T.nbase + pf_wrow<NMAT, PfTall::BN>((q >> 6) * 16)) >> 4;
         w_off[j] = (uint32_t)tile * (uint32_t)(K / 128) * 1024u + (uint32_t)(q & 63) * 16u;
       } else {
-        w_off[j] = (uint32_t)(T.nbase + pf_wrow<NMAT>(q >> 2)) * (uint32_t)(K / 2) + (uint32_t)(q & 3) * 16u;
+        w_off[j] = (uint32_t)(T.nbase + pf_wrow<NMAT, PfTall::BN>(q >> 2)) * (uint32_t)(K / 2) + (uint32_t)(q & 3) * 16u;
       }
     }
     const int s_n = W_NV ? (tid >> 1) : (tid & 255);
-    const uint32_t s_off = pf_scale_lane<TL, W_NV>(T.nbase + pf_wrow<NMAT>(s_n), tid & 1, K);
+    const uint32_t s_off = pf_scale_lane<TL, W_NV>(T.nbase + pf_wrow<NMAT, PfTall::BN>(s_n), tid & 1, K);
 
     auto fetch = [&](PfRegs& R, int kb) {
       R.a = bload128(ar, a_off + (uint32_t)kb * 64u, 0);
@@ -508,8 +539,8 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_nv_kernel(GemmArgs p)
     };
     auto store = [&](const PfRegs& R, uint8_t* st) {
       uint8_t* sa = st;
-      uint8_t* sw = st + kPfAStage;
-      uint8_t* ss = st + kPfAStage + kPfWStage;
+      uint8_t* sw = st + PfTall::AStage;
+      uint8_t* ss = st + PfTall::AStage + PfTall::WStage;
       const int row = tid >> 2, c = tid & 3;
       const float s_lo = e4m3_to_f32(R.asc & 0xFF) * p.a_gscale, s_hi = e4m3_to_f32((R.asc >> 8) & 0xFF) * p.a_gscale;
 #pragma unroll
@@ -531,7 +562,7 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_nv_kernel(GemmArgs p)
       for (int t = 0; t < 4; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     uint8_t* st0 = lds;
-    uint8_t* st1 = lds + kPfStage;
+    uint8_t* st1 = lds + PfTall::Stage;
     PfRegs R0, R1;
     __syncthreads();                                                 // previous tile done with LDS
     fetch(R0, 0);
@@ -544,13 +575,13 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_nv_kernel(GemmArgs p)
     for (int kb = 0; kb < nk; kb += 2) {
       fetch(R0, min(kb + 2, nk - 1));
       __builtin_amdgcn_sched_barrier(0);
-      if (active) pf_compute<NMAT, WF, TL>(st0, acc, wm, wn, li, lg);
+      if (active) pf_compute<NMAT, WF, TL, PfTall>(st0, acc, wm, wn, li, lg);
       __builtin_amdgcn_sched_barrier(0);
       store(R1, st1);                                                // step kb + 1
       __syncthreads();
       fetch(R1, min(kb + 3, nk - 1));
       __builtin_amdgcn_sched_barrier(0);
-      if (active) pf_compute<NMAT, WF, TL>(st1, acc, wm, wn, li, lg);
+      if (active) pf_compute<NMAT, WF, TL, PfTall>(st1, acc, wm, wn, li, lg);
       __builtin_amdgcn_sched_barrier(0);
       store(R0, st0);                                                // step kb + 2
       __syncthreads();
@@ -561,6 +592,9 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_nv_kernel(GemmArgs p)
 }
 
 // ------------------------------------------------------------------- host
+#ifndef MOE_PF_WIDE
+#define MOE_PF_WIDE 1          // bf16 tokens: 64 x 512 tiles where N allows
+#endif
 template <int NMAT, int WF, bool A_NV, bool TL>
 static void launch_prefill_one(const GemmArgs& a, hipStream_t stream) {
   // persistent: one workgroup per CU (8 waves); tiles are distributed on the device
@@ -568,12 +602,14 @@ static void launch_prefill_one(const GemmArgs& a, hipStream_t stream) {
     auto kern = gemm_prefill_nv_kernel<NMAT, WF, TL>;
     static bool attr_set = false;
     if (!attr_set) {
-      (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kPfStage);
+      (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * PfTall::Stage);
       attr_set = true;
     }
-    hipLaunchKernelGGL(kern, dim3(device_cus()), dim3(kPfThreads), 2 * kPfStage, stream, a);
+    hipLaunchKernelGGL(kern, dim3(device_cus()), dim3(kPfThreads), 2 * PfTall::Stage, stream, a);
+  } else if (a.N % (PfWide::BN / NMAT) == 0 && MOE_PF_WIDE) {
+    hipLaunchKernelGGL((gemm_prefill_dma_kernel<NMAT, WF, TL, PfWide>), dim3(device_cus()), dim3(kPfThreads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((gemm_prefill_dma_kernel<NMAT, WF, TL>), dim3(device_cus()), dim3(kPfThreads), 0, stream, a);
+    hipLaunchKernelGGL((gemm_prefill_dma_kernel<NMAT, WF, TL, PfTall>), dim3(device_cus()), dim3(kPfThreads), 0, stream, a);
   }
 }
 

@@ -10,7 +10,7 @@ template void prefill_run<false>(const GemmArgs&, bool, int, bool, hipStream_t);
 moe_status launch_gemm_decode(const GemmArgs&, bool swiglu, int wf, bool a_nv, int64_t rows, int persistent, hipStream_t);
 
 moe_status launch_gemm_prefill(const GemmArgs& a, bool swiglu, int wf, bool a_nv, int64_t rows, hipStream_t stream) {
-  const int bn = swiglu ? kPfBN / 2 : kPfBN;
+  const int bn = swiglu ? PfTall::BN / 2 : PfTall::BN;
   if (a.N % bn != 0 || a.K % (2 * kPfBK) != 0 || a.E > kPfMaxE) {
     // shapes the tiled kernels do not cover run on the weight-streaming kernel
     return launch_gemm_decode(a, swiglu, wf, a_nv, rows, 0, stream);

@@ -500,3 +500,36 @@ def test_grouped_gemm_tiled_is_bitwise_row_major(algo, fmt, general, amode):
         outs.append((host_bf16_bits(z), host_bf16_bits(o)))
     assert np.array_equal(outs[0][0], outs[1][0]), "gate/up differs between layouts"
     assert np.array_equal(outs[0][1], outs[1][1]), "down differs between layouts"
+
+
+@pytest.mark.parametrize("fmt", ["mx", "nv"])
+def test_grouped_gemm_prefill_narrow_n(fmt):
+    """Prefill tiles where N is a multiple of the 128 x 256 tile but not of the
+    64 x 512 one (SwiGLU N = 384, down N = 768): ragged experts, bf16 tokens."""
+    E, H, I = 8, 768, 384
+    counts = np.array(GEMM_COUNTS)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offsets[-1])
+    tsrc = 700
+    say(f"gemm prefill narrow-N fmt={fmt} R={R}")
+    x = synth.random_bf16(101, (tsrc, H))
+    gather = np.random.default_rng(102).integers(0, tsrc * 8, size=R).astype(np.int32)
+    wg, dg = _gemm_problem(103, E, I, H, counts, tsrc, fmt)
+    wu, du = _gemm_problem(104, E, I, H, counts, tsrc, fmt)
+    wd, dd = _gemm_problem(105, E, H, I, counts, R, fmt)
+    z = moe.grouped_gemm(dev_bf16(x), wg, wu, dev_i32(offsets), R, gather=dev_i32(gather), gather_div=8,
+                         algo=moe.MOE_ALGO_PREFILL)
+    z2 = synth.random_bf16(106, (R, I))
+    o = moe.grouped_gemm(dev_bf16(z2), wd, None, dev_i32(offsets), R, algo=moe.MOE_ALGO_PREFILL)
+    torch.cuda.synchronize()
+    a_val, z2v = bf16_to_f64(x), bf16_to_f64(z2)
+    zref = np.zeros((R, I))
+    oref = np.zeros((R, H))
+    for e in range(E):
+        rows = slice(offsets[e], offsets[e + 1])
+        a = a_val[gather[rows] // 8]
+        zref[rows] = oracle.silu(a @ dg[e].T) * (a @ du[e].T)
+        oref[rows] = z2v[rows] @ dd[e].T
+    zref = bf16_to_f64(oracle.round_to_bf16_bits(zref))
+    assert_close_rms(bf16_to_f64(host_bf16_bits(z)), zref, what="z", ulp_rel=BF16_ULP)
+    assert_close_rms(bf16_to_f64(host_bf16_bits(o)), oref, what="o", ulp_rel=BF16_ULP)
