@@ -43,15 +43,13 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
   return __uint_as_float(u);
 }
 
-// E4M3 (FN) byte -> float (exact).  0x7F / 0xFF -> NaN.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-  uint32_t e = (b >> 3) & 0xFu, m = b & 7u;
-  float normal = __uint_as_float(((e + 120u) << 23) | (m << 20));
-  float sub = (float)m * 0.001953125f;                              // m * 2^-9
-  float mag = (e == 0) ? sub : normal;                              // selects, no branches
-  mag = ((b & 0x7Fu) == 0x7Fu) ? __uint_as_float(0x7FC00000u) : mag;
-  return __uint_as_float(__float_as_uint(mag) | ((b & 0x80u) << 24));
-}
+// E4M3 (FN) -> float (exact; 0x7F / 0xFF -> NaN) by the gfx950 FP8 convert,
+// which decodes OCP E4M3 -- subnormals, signs and NaN included -- exactly like
+// the definition (checked for every byte value and byte position).
+// e4m3_to_f32: the low byte of b; e4m3_byte<SEL>: byte SEL of a word.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) { return __builtin_amdgcn_cvt_f32_fp8((int)b, 0); }
+template <int SEL>
+__device__ __forceinline__ float e4m3_byte(uint32_t w) { return __builtin_amdgcn_cvt_f32_fp8((int)w, SEL); }
 
 __device__ __forceinline__ bool is_pow2_scale(float s) {
   uint32_t u = __float_as_uint(s);

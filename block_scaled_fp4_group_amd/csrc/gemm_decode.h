@@ -116,8 +116,8 @@ struct DecodeWave {
     for (int m = 0; m < NMAT; ++m) {
       float s_lo, s_hi;
       if (W_NV) {
-        s_lo = e4m3_to_f32(sb[m] & 0xFF);
-        s_hi = e4m3_to_f32(sb[m] >> 8);
+        s_lo = e4m3_byte<0>(sb[m]);
+        s_hi = e4m3_byte<1>(sb[m]);
       } else {
         s_lo = s_hi = e8m0_to_f32(sb[m]);
       }
@@ -260,8 +260,8 @@ __device__ __forceinline__ void stage_rows(const GemmArgs& p, uint8_t* lds, int 
       const int64_t src = p.gather ? (int64_t)(p.gather[r] / p.gather_div) : r;
       u32x4 cw = *(const u32x4*)(p.a_data + src * (K / 2) + b * 16);
       uint32_t sw = *(const uint16_t*)(p.a_scales + src * (K / 16) + b * 2);
-      float s_lo = e4m3_to_f32(sw & 0xFF) * p.a_gscale;
-      float s_hi = e4m3_to_f32(sw >> 8) * p.a_gscale;
+      float s_lo = e4m3_byte<0>(sw) * p.a_gscale;
+      float s_hi = e4m3_byte<1>(sw) * p.a_gscale;
       u32x4* dst = (u32x4*)(lds + row * pitch + b * 64);
 #pragma unroll
       for (int s = 0; s < 4; ++s) dst[s] = __builtin_bit_cast(u32x4, fp4x8_to_bf16(cw[s], s < 2 ? s_lo : s_hi));

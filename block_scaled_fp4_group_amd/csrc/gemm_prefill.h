@@ -230,8 +230,8 @@ __device__ __forceinline__ void pf_compute(const uint8_t* st, f32x4 (&acc)[4][4]
     wq[g] = *(const u32x4*)(sw + (TL ? (uint32_t)(n >> 4) * 1024u + (uint32_t)(lg * 16 + li) * 16u : swz_w(n, lg)));
     if (W_NV) {
       const uint32_t b2 = *(const uint16_t*)(ss + n * 8 + lg * 2);
-      s_lo[g] = e4m3_to_f32(b2 & 0xFF);
-      s_hi[g] = e4m3_to_f32(b2 >> 8);
+      s_lo[g] = e4m3_byte<0>(b2);
+      s_hi[g] = e4m3_byte<1>(b2);
     } else {
       s_lo[g] = s_hi[g] = e8m0_to_f32(ss[n * 4 + lg]);
     }
@@ -542,7 +542,7 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_nv_kernel(GemmArgs p)
       uint8_t* sw = st + PfTall::AStage;
       uint8_t* ss = st + PfTall::AStage + PfTall::WStage;
       const int row = tid >> 2, c = tid & 3;
-      const float s_lo = e4m3_to_f32(R.asc & 0xFF) * p.a_gscale, s_hi = e4m3_to_f32((R.asc >> 8) & 0xFF) * p.a_gscale;
+      const float s_lo = e4m3_byte<0>(R.asc) * p.a_gscale, s_hi = e4m3_byte<1>(R.asc) * p.a_gscale;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
         *(u32x4*)(sa + swz_a(row, c * 4 + s)) = __builtin_bit_cast(u32x4, fp4x8_to_bf16(R.a[s], s < 2 ? s_lo : s_hi));
