@@ -215,9 +215,10 @@ struct PfNoHook {
 // of the next stage's loads there, between MFMAs).
 // TL: the weight stage holds each 16-row group as one 1 KB tiled block (lane
 // (li, lg) at 16 * (16 lg + li)) instead of swizzled rows.
-template <int NMAT, int WF, bool TL, typename SH, typename Hook = PfNoHook>
+// WREG: the weight codes come in registers (wreg[g]) instead of the LDS stage.
+template <int NMAT, int WF, bool TL, typename SH, bool WREG = false, typename Hook = PfNoHook>
 __device__ __forceinline__ void pf_compute(const uint8_t* st, f32x4 (&acc)[4][4], int wm, int wn, int li, int lg,
-                                           Hook&& hook = Hook()) {
+                                           Hook&& hook = Hook(), const u32x4* wreg = nullptr) {
   constexpr bool W_NV = WF != 0;
   const uint8_t* sa = st;
   const uint8_t* sw = st + SH::AStage;
@@ -227,7 +228,8 @@ __device__ __forceinline__ void pf_compute(const uint8_t* st, f32x4 (&acc)[4][4]
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int n = pf_lrow<NMAT, SH::BN>(wn, g) + li;
-    wq[g] = *(const u32x4*)(sw + (TL ? (uint32_t)(n >> 4) * 1024u + (uint32_t)(lg * 16 + li) * 16u : swz_w(n, lg)));
+    if (WREG) wq[g] = wreg[g];
+    else wq[g] = *(const u32x4*)(sw + (TL ? (uint32_t)(n >> 4) * 1024u + (uint32_t)(lg * 16 + li) * 16u : swz_w(n, lg)));
     if (W_NV) {
       const uint32_t b2 = *(const uint16_t*)(ss + n * 8 + lg * 2);
       s_lo[g] = e4m3_byte<0>(b2);
@@ -301,6 +303,10 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& p, const PfTile& T, 
 }
 
 // ------------------------------------------------ bf16 tokens: direct to LDS
+#ifndef MOE_PF_WREG
+#define MOE_PF_WREG 0          // 64 x 512 tiles: weight codes in registers, not LDS (the
+                               // compiler then drains all loads once per step: off)
+#endif
 template <int S>
 __device__ __forceinline__ uint8_t* pf_stage() {
   return S == 0 ? pf_stage0 : (S == 1 ? pf_stage1 : pf_stage2);
@@ -314,7 +320,12 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_dma_kernel(GemmArgs p
   __shared__ int s_wc[kPfThreads / kWave];
   // direct-to-LDS loads per wave and step: tokens (1 KB = 4 rows each), weight
   // codes (1 KB = 16 rows), scales (256 B: 64 MX rows or 32 NV rows)
-  constexpr int kA = SH::BM / 32, kW = SH::BN / 128;
+  // 64 x 512: every weight row belongs to one wave, so its codes go straight
+  // into that wave's registers (4 loads of 16 B per lane and step, three steps
+  // deep) instead of through LDS
+  constexpr bool WREG = MOE_PF_WREG && SH::BM == 64;
+  using WL = WeightLane<TL, W_NV>;
+  constexpr int kA = SH::BM / 32, kW = WREG ? 4 : SH::BN / 128;
   constexpr int kSRows = W_NV ? 32 : 64;                              // weight rows per scale load
   constexpr int kSLoads = SH::BN / kSRows;                            // scale loads per step (all waves)
   constexpr int kS = kSLoads > 8 ? kSLoads / 8 : 1;                   // per wave (MX 128 x 256: waves 4..7 repeat 0..3)
@@ -339,9 +350,6 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_dma_kernel(GemmArgs p
 
   for (int tile = t_begin; tile < t_end; tile += t_stride) {
     const PfTile T = locate_tile<NMAT, SH>(p, s_pref, tile);
-    // a wave whose 64 token rows all lie past the tile's end skips its MFMA
-    // work (its SIMD then runs the other wave alone); it still loads and syncs
-    const bool active = wm * 64 < T.mrows;
     float wglob[NMAT];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) wglob[m] = W_NV ? p.w_global[m][T.e] : 1.0f;
@@ -359,13 +367,22 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_dma_kernel(GemmArgs p
       a_off[i] = (uint32_t)(src * (int64_t)K * 2) + (uint32_t)chunk * 16u;   // < 2 GiB (checked on the host)
     }
     // weight codes: load j fills rows 16 * (kW wv + j) .. +15 (matrix wv / 4 for SwiGLU);
-    // tiled: that group's 1 KB block of the step, in lane order
+    // tiled: that group's 1 KB block of the step, in lane order.  WREG: load j
+    // is this wave's weight group j (rows lrow(wn, j) ..), row li, piece lg
     const int wmat = NMAT == 2 ? (wv >> 2) : 0;
     const uint8_t* w_base = p.w_packed[wmat] + T.e * mat_codes;
     uint32_t w_off[kW];
+    rsrc_t wrs[NMAT];
+    if (WREG) {
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) wrs[m] = make_rsrc(p.w_packed[m] + T.e * mat_codes, (uint32_t)mat_codes);
+    }
 #pragma unroll
     for (int j = 0; j < kW; ++j) {
-      if (TL) {
+      if (WREG) {
+        const int R = T.nbase + pf_wrow<NMAT, SH::BN>(pf_lrow<NMAT, SH::BN>(wn, j));
+        w_off[j] = (uint32_t)R * (uint32_t)(K / 2) + WL::code(li, lg, K);
+      } else if (TL) {
         const int tile = (T.nbase + pf_wrow<NMAT, SH::BN>((wv * kW + j) * 16)) >> 4;
         w_off[j] = (uint32_t)tile * (uint32_t)(K / 128) * 1024u + (uint32_t)lane * 16u;
       } else {
@@ -387,16 +404,24 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_dma_kernel(GemmArgs p
       s_off[h] = pf_scale_lane<TL, W_NV>(T.nbase + pf_wrow<NMAT, SH::BN>(s_n), lane & 1, K);
     }
 
+    u32x4 wring[3][4];                                               // WREG: codes of steps k .. k + 2
     // load q of step kb into stage S: kA token loads, kW weight-code loads, kS scale loads
     auto issue_one = [&](auto S_tag, int kb, int q) {
-      uint8_t* st = pf_stage<decltype(S_tag)::value>();
-      if (q < kA) {
-        __builtin_amdgcn_global_load_lds((const void*)(p.a_data + kb * 256 + a_off[q]),
-                                         (lds_void_t*)(st + (wv * kA + q) * 1024), 16, 0, 0);
-      } else if (q < kA + kW) {
-        const int j = q - kA;
-        __builtin_amdgcn_global_load_lds((const void*)(w_base + kb * (TL ? 1024 : 64) + w_off[j]),
-                                         (lds_void_t*)(st + SH::AStage + (wv * kW + j) * 1024), 16, 0, 0);
+      constexpr int S = decltype(S_tag)::value;
+      uint8_t* st = pf_stage<S>();
+      // (WREG: the register loads go first, then the direct-to-LDS ones)
+      constexpr int qa = WREG ? kW : 0, qw = WREG ? 0 : kA;
+      if (q >= qa && q < qa + kA) {
+        __builtin_amdgcn_global_load_lds((const void*)(p.a_data + kb * 256 + a_off[q - qa]),
+                                         (lds_void_t*)(st + (wv * kA + q - qa) * 1024), 16, 0, 0);
+      } else if (q >= qw && q < qw + kW) {
+        const int j = q - qw;
+        if (WREG) {
+          wring[S][j] = bload128(wrs[NMAT == 2 ? (j >> 1) : 0], w_off[j] + (uint32_t)kb * WL::kStep, 0);
+        } else {
+          __builtin_amdgcn_global_load_lds((const void*)(w_base + kb * (TL ? 1024 : 64) + w_off[j]),
+                                           (lds_void_t*)(st + SH::AStage + (wv * kW + j) * 1024), 16, 0, 0);
+        }
       } else {
         const int h = q - kA - kW;
         __builtin_amdgcn_global_load_lds((const void*)(s_base[h] + pf_scale_step<TL, W_NV>(kb) + s_off[h]),
@@ -431,11 +456,10 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_dma_kernel(GemmArgs p
         if (2 * s < kDmaPerStep) issue_one(SN, kn, 2 * s);
         if (2 * s + 1 < kDmaPerStep) issue_one(SN, kn, 2 * s + 1);
       };
-      if (active) {
-        pf_compute<NMAT, WF, TL, SH>(pf_stage<S>(), acc, wm, wn, li, lg, hook);
-      } else {
-        issue(SN, kn);
-      }
+      // every wave computes, also on rows past the tile's end (their outputs
+      // are not stored): a branch here made the compiler drain every load in
+      // flight before each step's first LDS read, losing the two-step lead
+      pf_compute<NMAT, WF, TL, SH, WREG>(pf_stage<S>(), acc, wm, wn, li, lg, hook, wring[S]);
     };
 
     __syncthreads();                                                 // previous tile done with the stages
@@ -452,6 +476,9 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_dma_kernel(GemmArgs p
 
     pf_epilogue<NMAT>(p, T, acc, wglob, wm, wn, li, lg);
   }
+  // the last tile leaves its unread repeat loads in flight: let them land
+  // before the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));             // vmcnt(0)
 }
 
 // --------------------------------------- NVFP4 tokens: through registers
