@@ -1,6 +1,8 @@
 """Build the gfx950 shared library in-tree with hipcc (no torch involved).
 
-    python -m block_scaled_fp4_group_amd.build
+    python block_scaled_fp4_group_amd/build.py
+
+(run as a script: importing the package itself needs the built library)
 
 Each HIP source compiles to its own object in parallel (the GEMM files hold
 many kernel instantiations), then one link step writes libmoefp4.so.
