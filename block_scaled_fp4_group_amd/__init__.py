@@ -53,7 +53,7 @@ class Out(ctypes.Structure):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m block_scaled_fp4_group_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python block_scaled_fp4_group_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH, mode=ctypes.RTLD_LOCAL)
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     lib.moe_status_string.restype = ctypes.c_char_p
