@@ -658,10 +658,7 @@ static void launch_persist_one(const GemmArgs& a, hipStream_t stream) {
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     attr_set = true;
   }
-#ifndef MOE_DEC_PERSIST_GRID
-#define MOE_DEC_PERSIST_GRID 1
-#endif
-  hipLaunchKernelGGL(kern, dim3(device_cus() * persist_wg_per_cu(NMAT, NS) * MOE_DEC_PERSIST_GRID), dim3(kPsWaves * 64), lds, stream, a);
+  hipLaunchKernelGGL(kern, dim3(device_cus() * persist_wg_per_cu(NMAT, NS)), dim3(kPsWaves * 64), lds, stream, a);
 }
 
 template <bool TL, int NMAT, int NS>

@@ -521,7 +521,9 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_nv_kernel(GemmArgs p)
 
   for (int tile = t_begin; tile < t_end; tile += t_stride) {
     const PfTile T = locate_tile<NMAT, PfTall>(p, s_pref, tile);
-    const bool active = wm * 64 < T.mrows;                           // as in the bf16 kernel
+    // a wave whose 64 token rows all lie past the tile's end skips its MFMAs;
+    // it still fetches, stores and syncs (the barriers here wait for every load anyway)
+    const bool active = wm * 64 < T.mrows;
     rsrc_t wr[NMAT], sr[NMAT];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
