@@ -8,6 +8,9 @@ resident in HBM.  The headline workload is the decode shape (256 experts in 8
 groups, keep 4 groups, top-8, hidden 4096, expert intermediate 2048, W4A16
 MXFP4) at a batch of 64 tokens; decode timings rotate four independent layer
 weight sets so the 256 MB Infinity Cache cannot serve repeated weight reads.
+The headline step is the layer replayed from a captured HIP graph (one graph
+per weight set); the eager step time is reported beside it, and the dominant
+kernel's time comes from HIP events around its launch in the eager steps.
 The JSON line also carries the batch-1/8 decode lines, the prefill, W4A4 and
 REAP-50 shapes, the roofline of the dominant kernel (the gate/up GEMM) and the
 CPU oracle timed on a bounded sample.
@@ -224,9 +227,10 @@ def main():
         return dict(T=T, ms=ms, gate_up_ms=k_ms, graph_ms=g_ms, D=D, x=x, l=l, layers=layers)
 
     log("[bench] decode T=64 (headline)")
-    main_r = decode_line(64, args.steps, args.warmup)
+    main_r = decode_line(64, args.steps, args.warmup, graph=True)
     T = 64
-    tok_s = T / (main_r["ms"] / 1e3)
+    step_ms = main_r["graph_ms"]            # the layer step replayed from a captured HIP graph
+    tok_s = T / (step_ms / 1e3)
     gu_bytes = gate_up_bytes(main_r["D"], T, s)
     achieved = gu_bytes / (main_r["gate_up_ms"] / 1e3) / 1e9
     lb = layer_bytes(main_r["D"], T, s)
@@ -239,7 +243,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(main_r["ms"], 4),
+        "ms_per_step": round(step_ms, 4),
+        "ms_per_step_eager": round(main_r["ms"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -256,7 +261,7 @@ def main():
                      "kernel": "gemm_decode_kernel (gate/up + SwiGLU" + (", tiled weights)" if TILED else ")"),
                      "kernel_ms": round(main_r["gate_up_ms"], 5),
                      "algorithmic_bytes": int(gu_bytes)},
-        "layer_hbm_frac": round(lb / (main_r["ms"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "layer_hbm_frac": round(lb / (step_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
     }
     extras = {}
     if not args.no_extras:
