@@ -31,6 +31,10 @@ size_t permute_ws_bytes(int64_t R, int E) {
   return (size_t)blocks * (size_t)E * sizeof(int32_t);
 }
 
+// Sub-chunk q of wave w: interleaved over the waves, so a short chunk (a
+// decode batch) still spreads its slots over every wave.
+__device__ __forceinline__ int sub_of(int w, int q) { return q * (kPermThreads / kWave) + w; }
+
 // Ranks of this wave's 8 sub-chunks: expert id (-1 when absent/invalid), rank
 // among equal ids inside the 64-slot sub-chunk, and the group size.
 struct SubRanks {
@@ -42,19 +46,31 @@ struct SubRanks {
 __device__ __forceinline__ void rank_subchunks(const int32_t* __restrict__ ids, int64_t R, int E, int nbits,
                                                int64_t base, SubRanks& r) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // all of the wave's loads in flight before the first is used (slots past R
+  // read slot base instead; an empty chunk, R = 0, reads nothing)
+  int v[kSubPerWave];
+  if (R > base) {
+#pragma unroll
+    for (int q = 0; q < kSubPerWave; ++q) {
+      const int64_t s = base + (int64_t)sub_of(w, q) * kWave + lane;
+      v[q] = ids[s < R ? s : base];
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < kSubPerWave; ++q) v[q] = -1;
+  }
 #pragma unroll
   for (int q = 0; q < kSubPerWave; ++q) {
-    int sub = w * kSubPerWave + q;
-    int64_t s = base + (int64_t)sub * kWave + lane;
-    int e = -1;
-    if (s < R) {
-      int v = ids[s];
-      if (v >= 0 && v < E) e = v;
-    }
+    const int64_t s = base + (int64_t)sub_of(w, q) * kWave + lane;
+    const int e = (s < R && v[q] >= 0 && v[q] < E) ? v[q] : -1;
+    // lanes of an absent slot (e = -1, every bit set) stay out of every valid
+    // lane's peers through the first ballot; their own ranks are never used.
+    // A sub-chunk with no slot (past R) skips the bit ballots.
     uint64_t peers = __ballot(e >= 0);
-    for (int b = 0; b < nbits; ++b) {
-      uint64_t m = __ballot(e >= 0 && ((e >> b) & 1));
-      peers &= ((e >> b) & 1) ? m : ~m;
+    for (int b = 0; b < nbits && peers != 0; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
     }
     r.e[q] = e;
     r.rank[q] = __popcll(peers & ((1ull << lane) - 1ull));
@@ -73,7 +89,7 @@ __device__ __forceinline__ void subchunk_prefix(const SubRanks& r, int e0, uint1
 #pragma unroll
   for (int q = 0; q < kSubPerWave; ++q) {
     int e = r.e[q];
-    if (e >= e0 && e < e0 + kERange && r.rank[q] == 0) cnt[w * kSubPerWave + q][e - e0] = (uint16_t)r.size[q];
+    if (e >= e0 && e < e0 + kERange && r.rank[q] == 0) cnt[sub_of(w, q)][e - e0] = (uint16_t)r.size[q];
     // (a sub-chunk past nsub holds no slot, so e < 0 there and nothing is written)
   }
   __syncthreads();
@@ -97,8 +113,8 @@ __device__ __forceinline__ void write_rows(const SubRanks& r, int e0, const uint
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
   for (int q = 0; q < kSubPerWave; ++q) {
-    int sub = w * kSubPerWave + q;
-    int64_t s = base + (int64_t)sub * kWave + lane;
+    const int sub = sub_of(w, q);
+    const int64_t s = base + (int64_t)sub * kWave + lane;
     int e = r.e[q];
     if (e >= e0 && e < e0 + kERange) {
       int32_t pos = ebase[e - e0] + (int32_t)cnt[sub][e - e0] + r.rank[q];

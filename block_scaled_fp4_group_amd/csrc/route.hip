@@ -11,13 +11,15 @@
 // load of the logits row is coalesced.  The reductions run in registers:
 // within a row of 16 lanes with DPP moves (quad permutes, half-row and row
 // mirrors), across rows with the gfx950 16- and 32-lane swaps, so a wave-wide
-// argmax costs a few dozen cycles per level instead of an LDS round trip.
+// maximum costs a few dozen cycles per level instead of an LDS round trip.
 //   * group score (sum of the two largest biased scores): a segmented top-2
 //     merge over the group's lanes when the group size is a power of two, an
 //     LDS scan otherwise;
 //   * kept groups: every lane ranks the group scores (ties to the lower index);
-//   * experts: top_k rounds of a wave argmax over (score, index), ties to the
-//     lower index.
+//   * experts: top_k rounds of a wave-wide maximum over order-preserving
+//     64-bit keys of the biased scores, then the lowest expert index holding
+//     that key (ties to the lower index) from one ballot per register.
+// All loads of a row are issued before any of them is used.
 #include "common.h"
 
 namespace moe {
@@ -59,24 +61,33 @@ __device__ __forceinline__ double partner_f64(double x) {
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
-// ---- (value, index) argmax: larger value wins, equal values go to the lower
-// index, index -1 is empty
-__device__ __forceinline__ void argmax_merge(double& v, int& i, double ov, int oi) {
-  const bool take = (oi >= 0) && (i < 0 || ov > v || (ov == v && oi < i));
-  v = take ? ov : v;
-  i = take ? oi : i;
+// ---- order-preserving keys: for doubles that are not NaN, x > y exactly when
+// key(x) > key(y), and equal values get equal keys (a biased score is never
+// -0, since a sigmoid is >= +0).  Key 0 is below every real key: "no candidate".
+__device__ __forceinline__ uint64_t order_key(double x) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
 }
 template <int L>
-__device__ __forceinline__ void argmax_level(double& v, int& i) {
-  argmax_merge(v, i, partner_f64<L>(v), partner_i32<L>(i));
+__device__ __forceinline__ uint64_t partner_u64(uint64_t x) {
+  const uint32_t lo = (uint32_t)partner_i32<L>((int)(uint32_t)x);
+  const uint32_t hi = (uint32_t)partner_i32<L>((int)(uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
 }
-__device__ __forceinline__ void wave_argmax(double& v, int& i) {
-  argmax_level<0>(v, i);
-  argmax_level<1>(v, i);
-  argmax_level<2>(v, i);
-  argmax_level<3>(v, i);
-  argmax_level<4>(v, i);
-  argmax_level<5>(v, i);
+template <int L>
+__device__ __forceinline__ void max_level(uint64_t& k) {
+  const uint64_t o = partner_u64<L>(k);
+  k = o > k ? o : k;
+}
+// every lane gets the wave's largest key
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+  max_level<0>(k);
+  max_level<1>(k);
+  max_level<2>(k);
+  max_level<3>(k);
+  max_level<4>(k);
+  max_level<5>(k);
+  return k;
 }
 
 // ---- top-2 of a multiset as (b1 >= b2); merging two disjoint halves
@@ -115,18 +126,24 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   const bool pow2 = (gs & (gs - 1)) == 0;
   const float* lrow = logits + t * E;
 
+  // every load in flight at once (lanes past E read expert E - 1 and drop it)
+  float lv[kRouteMaxPer], bv[kRouteMaxPer];
+#pragma unroll
+  for (int j = 0; j < kRouteMaxPer; ++j) lv[j] = lrow[min(lane + 64 * j, E - 1)];
+  if (bias) {
+#pragma unroll
+    for (int j = 0; j < kRouteMaxPer; ++j) bv[j] = bias[min(lane + 64 * j, E - 1)];
+  } else {
+#pragma unroll
+    for (int j = 0; j < kRouteMaxPer; ++j) bv[j] = 0.0f;
+  }
   double s[kRouteMaxPer], c[kRouteMaxPer];
 #pragma unroll
   for (int j = 0; j < kRouteMaxPer; ++j) {
-    const int e = lane + 64 * j;
-    if (e < E) {
-      const double l = (double)lrow[e];
-      s[j] = 1.0 / (1.0 + exp(-l));
-      c[j] = s[j] + (bias ? (double)bias[e] : 0.0);
-    } else {
-      s[j] = 0.0;
-      c[j] = -INFINITY;
-    }
+    const bool in = lane + 64 * j < E;
+    const double sg = 1.0 / (1.0 + exp(-(double)lv[j]));
+    s[j] = in ? sg : 0.0;
+    c[j] = in ? sg + (double)bv[j] : -INFINITY;
   }
 
   // ---- group scores -> gscore[wv][g]
@@ -187,34 +204,38 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   const uint64_t kept = __ballot(keep);
 
   // ---- top_k experts among the kept groups
-  bool elig[kRouteMaxPer];
+  uint64_t key[kRouteMaxPer];
 #pragma unroll
   for (int j = 0; j < kRouteMaxPer; ++j) {
     const int e = lane + 64 * j;
-    elig[j] = (e < E) && ((kept >> (e / gs)) & 1ull);
+    const bool elig = (e < E) && ((kept >> (e / gs)) & 1ull);
+    key[j] = elig ? order_key(c[j]) : 0ull;
   }
   double sel_s = 0.0, tot = 0.0;     // lane r < top_k keeps the r-th pick
   int sel_e = 0;
   for (int r = 0; r < top_k; ++r) {
-    double v = -INFINITY;
-    int i = -1;
+    uint64_t m = key[0];
 #pragma unroll
-    for (int j = 0; j < kRouteMaxPer; ++j)
-      if (elig[j] && (i < 0 || c[j] > v)) { v = c[j]; i = lane + 64 * j; }
-    wave_argmax(v, i);
-    // every lane now holds the pick; its owner supplies the unbiased score
-    const int pick = __builtin_amdgcn_readfirstlane(i);
-    double sv = 0.0;
+    for (int j = 1; j < kRouteMaxPer; ++j) m = key[j] > m ? key[j] : m;
+    m = wave_max_key(m);
+    // the lowest expert index whose key is the maximum (a uniform value)
+    int pick = 0;
 #pragma unroll
-    for (int j = 0; j < kRouteMaxPer; ++j) {
-      const bool mine = lane + 64 * j == pick;
-      sv = mine ? s[j] : sv;
-      elig[j] = elig[j] && !mine;
+    for (int j = kRouteMaxPer - 1; j >= 0; --j) {
+      const uint64_t hit = __ballot((key[j] == m) & (lane + 64 * j < E));
+      pick = hit ? 64 * j + __ffsll((long long)hit) - 1 : pick;
     }
-    const uint64_t su = (uint64_t)__double_as_longlong(sv);
-    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)su, pick & 63);
-    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(su >> 32), pick & 63);
-    sv = __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+    const int pl = pick & 63, pj = pick >> 6;
+    // its owner lane supplies the unbiased score; the pick leaves the candidates
+    double sj = s[0];
+#pragma unroll
+    for (int j = 1; j < kRouteMaxPer; ++j) sj = pj == j ? s[j] : sj;
+#pragma unroll
+    for (int j = 0; j < kRouteMaxPer; ++j) key[j] = ((pj == j) & (lane == pl)) ? 0ull : key[j];
+    const uint64_t su = (uint64_t)__double_as_longlong(sj);
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)su, pl);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(su >> 32), pl);
+    const double sv = __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
     tot += sv;                                     // sum in pick order
     if (lane == r) { sel_s = sv; sel_e = pick; }
   }
