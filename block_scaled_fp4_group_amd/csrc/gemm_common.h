@@ -48,24 +48,36 @@ struct WeightLane {
 
 // Locate the j-th expert with at least one row (experts in index order).
 // Returns false when fewer than j+1 experts are active.  All threads of the
-// block must call it.
+// block must call it.  The thread that finds the expert also hands over its
+// row range, so no second offsets load follows the search.
 __device__ __forceinline__ bool find_active_expert(const int32_t* __restrict__ offsets, int E, int64_t rows, int j,
                                                    int& e_out, int& r0, int& r1) {
-  __shared__ int s_e;
+  __shared__ int s_found[3];                                  // expert, first row, end row
   __shared__ int s_wc[16];
   const int nthr = blockDim.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = nthr >> 6;
-  if (threadIdx.x == 0) s_e = -1;
+  if (threadIdx.x == 0) s_found[0] = -1;
   int running = 0;
   for (int e0 = 0; e0 < E; e0 += nthr) {
-    int e = e0 + threadIdx.x;
-    bool act = e < E && offsets[e + 1] > offsets[e];
+    const int e = e0 + threadIdx.x;
+    int o0 = 0, o1 = 0;
+    if (e < E) {
+      o0 = offsets[e];
+      o1 = offsets[e + 1];
+    }
+    const bool act = o1 > o0;
     uint64_t b = __ballot(act);
     if (lane == 0) s_wc[w] = __popcll(b);
     __syncthreads();
     int before = running;
     for (int i = 0; i < w; ++i) before += s_wc[i];
     int rank = before + __popcll(b & ((1ull << lane) - 1ull));
-    if (act && rank == j) s_e = e;
+    if (act && rank == j) {
+      // rows outside [0, rows) are never touched, whatever the offsets hold
+      const int c0 = (int)max((int64_t)0, min((int64_t)o0, rows));
+      s_found[0] = e;
+      s_found[1] = c0;
+      s_found[2] = (int)max((int64_t)c0, min((int64_t)o1, rows));
+    }
     int tot = 0;
     for (int i = 0; i < nw; ++i) tot += s_wc[i];
     running += tot;
@@ -73,12 +85,11 @@ __device__ __forceinline__ bool find_active_expert(const int32_t* __restrict__ o
     if (running > j) break;
   }
   __syncthreads();
-  int e = s_e;
+  const int e = s_found[0];
   if (e < 0) return false;
   e_out = e;
-  // rows outside [0, rows) are never touched, whatever the offsets hold
-  r0 = (int)max((int64_t)0, min((int64_t)offsets[e], rows));
-  r1 = (int)max((int64_t)r0, min((int64_t)offsets[e + 1], rows));
+  r0 = s_found[1];
+  r1 = s_found[2];
   return r1 > r0;
 }
 
