@@ -24,7 +24,7 @@ MOE_EPI_NONE, MOE_EPI_SWIGLU = 0, 1
 MOE_ALGO_AUTO, MOE_ALGO_DECODE, MOE_ALGO_PREFILL, MOE_ALGO_DECODE_PERSISTENT = 0, 1, 2, 3
 
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_version", "moe_route", "moe_permute_workspace_bytes",
-           "moe_permute", "moe_fp4_grouped_gemm", "moe_combine", "fp4_transcode_mx_to_nv", "moe_quantize_nvfp4",
+           "moe_permute", "moe_route_permute", "moe_fp4_grouped_gemm", "moe_combine", "fp4_transcode_mx_to_nv", "moe_quantize_nvfp4",
            "moe_fp4_tile_weights")
 
 
@@ -68,6 +68,8 @@ def _load() -> ctypes.CDLL:
     lib.moe_permute_workspace_bytes.argtypes = [i64, i32, i32]
     lib.moe_permute.restype = i32
     lib.moe_permute.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.moe_route_permute.restype = i32
+    lib.moe_route_permute.argtypes = [vp, vp, i64, ctypes.POINTER(RouteParams), vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_fp4_grouped_gemm.restype = i32
     lib.moe_fp4_grouped_gemm.argtypes = [ctypes.POINTER(Act), ctypes.POINTER(Fp4Weights), ctypes.POINTER(Fp4Weights),
                                          i32, vp, i64, ctypes.POINTER(Out), i32, vp]
@@ -144,6 +146,34 @@ def permute(ids: torch.Tensor, num_experts: int, workspace: Optional[torch.Tenso
     _check(lib.moe_permute(_ptr(ids), T, top_k, num_experts, _ptr(offsets), _ptr(sorted_slots), _ptr(slot_rows),
                            _ptr(workspace), workspace.numel(), _stream(stream)), "moe_permute")
     return offsets, sorted_slots, slot_rows
+
+
+def route_permute(logits: torch.Tensor, bias: Optional[torch.Tensor], num_experts: int, n_group: int,
+                  topk_group: int, top_k: int, routed_scaling_factor: float, counter: torch.Tensor,
+                  norm_topk_prob: bool = True, ids=None, weights=None, workspace: Optional[torch.Tensor] = None,
+                  offsets=None, sorted_slots=None, slot_rows=None, stream=None):
+    """route() then permute() of its ids, in one launch for up to 2048 slots.
+    ``counter``: one int32 on the device, zero before the first call (each call
+    leaves it zero); calls sharing it must not overlap."""
+    _dev(logits, "logits")
+    _dev(counter, "counter")
+    if counter.dtype != torch.int32 or counter.numel() < 1:
+        raise ValueError("counter must hold one int32")
+    T = logits.shape[0]
+    dev = logits.device
+    R = T * top_k
+    ids = torch.empty((T, top_k), dtype=torch.int32, device=dev) if ids is None else ids
+    weights = torch.empty((T, top_k), dtype=torch.float32, device=dev) if weights is None else weights
+    offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
+    sorted_slots = torch.empty(R, dtype=torch.int32, device=dev) if sorted_slots is None else sorted_slots
+    slot_rows = torch.empty(R, dtype=torch.int32, device=dev) if slot_rows is None else slot_rows
+    if workspace is None:
+        workspace = torch.empty(max(permute_workspace_bytes(T, top_k, num_experts), 16), dtype=torch.uint8, device=dev)
+    p = RouteParams(num_experts, n_group, topk_group, top_k, routed_scaling_factor, int(norm_topk_prob))
+    _check(lib.moe_route_permute(_ptr(logits), _ptr(bias), T, ctypes.byref(p), _ptr(ids), _ptr(weights),
+                                 _ptr(offsets), _ptr(sorted_slots), _ptr(slot_rows), _ptr(counter), _ptr(workspace),
+                                 workspace.numel(), _stream(stream)), "moe_route_permute")
+    return ids, weights, offsets, sorted_slots, slot_rows
 
 
 @dataclasses.dataclass

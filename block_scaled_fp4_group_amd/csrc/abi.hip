@@ -28,6 +28,9 @@ moe_status launch_status(const char* what) {
 moe_status launch_route(const float*, const float*, int64_t, const moe_route_params*, int32_t*, float*, hipStream_t);
 size_t permute_ws_bytes(int64_t R, int E);
 moe_status launch_permute(const int32_t*, int64_t, int, int, int32_t*, int32_t*, int32_t*, void*, hipStream_t);
+bool route_permute_fits(int64_t T, int top_k);
+moe_status launch_route_permute(const float*, const float*, int64_t, const moe_route_params*, int32_t*, float*, int32_t*,
+                                int32_t*, int32_t*, uint32_t*, hipStream_t);
 moe_status launch_combine(const void*, const int32_t*, const float*, const void*, int64_t, int, int, void*, hipStream_t);
 moe_status launch_transcode(const uint8_t*, const uint8_t*, int64_t, int, int, uint8_t*, float*, int64_t*, hipStream_t);
 moe_status launch_quant(const void*, int64_t, int, float, uint8_t*, uint8_t*, void*, hipStream_t);
@@ -73,9 +76,7 @@ const char* moe_last_error(void) { return g_err; }
 
 const char* moe_version(void) { return "moe_fp4 gfx950 1.0"; }
 
-moe_status moe_route(const float* logits, const float* correction_bias, int64_t T, const moe_route_params* p,
-                     int32_t* topk_ids, float* topk_weights, hipStream_t stream) {
-  g_err[0] = 0;
+static moe_status check_route(const moe_route_params* p, int64_t T) {
   MOE_CHECK(p != nullptr, "moe_route: params is NULL");
   MOE_CHECK(T >= 0, "moe_route: T < 0");
   const int E = p->num_experts;
@@ -85,6 +86,14 @@ moe_status moe_route(const float* logits, const float* correction_bias, int64_t 
   MOE_CHECK(p->topk_group >= 1 && p->topk_group <= p->n_group, "moe_route: bad topk_group %d", p->topk_group);
   MOE_CHECK(p->top_k >= 1 && p->top_k <= 16 && p->top_k <= p->topk_group * (E / p->n_group),
             "moe_route: bad top_k %d", p->top_k);
+  return MOE_OK;
+}
+
+moe_status moe_route(const float* logits, const float* correction_bias, int64_t T, const moe_route_params* p,
+                     int32_t* topk_ids, float* topk_weights, hipStream_t stream) {
+  g_err[0] = 0;
+  const moe_status st = check_route(p, T);
+  if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   MOE_CHECK(logits && topk_ids && topk_weights, "moe_route: NULL pointer");
   return launch_route(logits, correction_bias, T, p, topk_ids, topk_weights, stream);
@@ -112,6 +121,37 @@ moe_status moe_permute(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_
     }
   }
   return launch_permute(topk_ids, T, top_k, num_experts, expert_offsets, sorted_slots, slot_rows, workspace, stream);
+}
+
+moe_status moe_route_permute(const float* logits, const float* correction_bias, int64_t T, const moe_route_params* p,
+                             int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets, int32_t* sorted_slots,
+                             int32_t* slot_rows, uint32_t* counter, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  g_err[0] = 0;
+  const moe_status st = check_route(p, T);
+  if (st != MOE_OK) return st;
+  if (!route_permute_fits(T, p->top_k)) {
+    // two launches; every argument of both is checked before the first
+    MOE_CHECK(expert_offsets != nullptr, "moe_route_permute: expert_offsets is NULL");
+    if (T > 0) {
+      MOE_CHECK(logits && topk_ids && topk_weights && sorted_slots && slot_rows, "moe_route_permute: NULL pointer");
+      MOE_CHECK(T * (int64_t)p->top_k < ((int64_t)1 << 31), "moe_route_permute: too many slots");
+      const size_t need = permute_ws_bytes(T * p->top_k, p->num_experts);
+      if (workspace_bytes < need || workspace == nullptr) {
+        set_error("moe_route_permute: workspace %zu bytes < %zu", workspace_bytes, need);
+        return MOE_ERR_WORKSPACE;
+      }
+      const moe_status rs = launch_route(logits, correction_bias, T, p, topk_ids, topk_weights, stream);
+      if (rs != MOE_OK) return rs;
+    }
+    return moe_permute(topk_ids, T, p->top_k, p->num_experts, expert_offsets, sorted_slots, slot_rows, workspace,
+                       workspace_bytes, stream);
+  }
+  MOE_CHECK(logits && topk_ids && topk_weights && expert_offsets && sorted_slots && slot_rows && counter,
+            "moe_route_permute: NULL pointer");
+  MOE_CHECK(((uintptr_t)counter & 3) == 0, "moe_route_permute: counter not 4-byte aligned");
+  return launch_route_permute(logits, correction_bias, T, p, topk_ids, topk_weights, expert_offsets, sorted_slots,
+                              slot_rows, counter, stream);
 }
 
 static moe_status check_weights(const moe_fp4_weights* w, const char* name) {

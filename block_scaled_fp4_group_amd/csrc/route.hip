@@ -20,7 +20,7 @@
 //     64-bit keys of the biased scores, then the lowest expert index holding
 //     that key (ties to the lower index) from one ballot per register.
 // All loads of a row are issued before any of them is used.
-#include "common.h"
+#include "permute.h"
 
 namespace moe {
 
@@ -110,11 +110,13 @@ __device__ __forceinline__ void top2_segment(double& b1, double& b2, int levels)
   if (levels > 5) top2_level<5>(b1, b2);
 }
 
-__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits,
-                                                    const float* __restrict__ bias, int64_t T, int E,
-                                                    int n_group, int topk_group, int top_k, float scale,
-                                                    int norm, int32_t* __restrict__ ids,
-                                                    float* __restrict__ weights) {
+// The kRouteWaves tokens of this block, one per wave.  All threads of the
+// block must call it (it synchronises the block).
+static_assert(kPermThreads == 256, "the router block runs the permutation");
+
+__device__ __forceinline__ void route_tokens(const float* __restrict__ logits, const float* __restrict__ bias,
+                                             int64_t T, int E, int n_group, int topk_group, int top_k, float scale,
+                                             int norm, int32_t* __restrict__ ids, float* __restrict__ weights) {
   __shared__ double gscore[kRouteWaves][64];
   __shared__ double cval[kRouteWaves][256];
   const int lane = threadIdx.x & 63;
@@ -246,6 +248,42 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   }
 }
 
+__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits,
+                                                    const float* __restrict__ bias, int64_t T, int E,
+                                                    int n_group, int topk_group, int top_k, float scale,
+                                                    int norm, int32_t* __restrict__ ids,
+                                                    float* __restrict__ weights) {
+  route_tokens(logits, bias, T, E, n_group, topk_group, top_k, scale, norm, ids, weights);
+}
+
+// Router and permutation in one launch (R = T * top_k <= kPermChunk).  Each
+// block routes its tokens, then adds one to *counter; the block that brings
+// it to gridDim.x has every block's ids behind it and runs the permutation,
+// then sets the counter back to zero for the next launch.  The fences are
+// device-scope release (each thread, after its stores) and acquire (the last
+// block, before its loads): the blocks sit on different XCDs, whose L2 caches
+// are not coherent with each other.
+__global__ __launch_bounds__(256) void route_permute_kernel(const float* __restrict__ logits,
+                                                            const float* __restrict__ bias, int64_t T, int E,
+                                                            int n_group, int topk_group, int top_k, float scale,
+                                                            int norm, int32_t* __restrict__ ids,
+                                                            float* __restrict__ weights, int nbits,
+                                                            int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ sorted_slots,
+                                                            int32_t* __restrict__ slot_rows,
+                                                            uint32_t* __restrict__ counter) {
+  __shared__ int s_last;
+  route_tokens(logits, bias, T, E, n_group, topk_group, top_k, scale, norm, ids, weights);
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicAdd(counter, 1u) == gridDim.x - 1;
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  permute_one_chunk(ids, T * top_k, E, nbits, offsets, sorted_slots, slot_rows);
+  if (threadIdx.x == 0) atomicExch(counter, 0u);
+}
+
 moe_status launch_route(const float* logits, const float* bias, int64_t T, const moe_route_params* p,
                         int32_t* ids, float* weights, hipStream_t stream) {
   if (T == 0) return MOE_OK;
@@ -254,6 +292,20 @@ moe_status launch_route(const float* logits, const float* bias, int64_t T, const
                      p->num_experts, p->n_group, p->topk_group, p->top_k, p->routed_scaling_factor,
                      p->norm_topk_prob, ids, weights);
   return launch_status("moe_route");
+}
+
+bool route_permute_fits(int64_t T, int top_k) { return T >= 1 && T * top_k <= kPermChunk; }
+
+moe_status launch_route_permute(const float* logits, const float* bias, int64_t T, const moe_route_params* p,
+                                int32_t* ids, float* weights, int32_t* offsets, int32_t* sorted_slots,
+                                int32_t* slot_rows, uint32_t* counter, hipStream_t stream) {
+  int nbits = 0;
+  while ((1 << nbits) < p->num_experts) ++nbits;
+  const int64_t blocks = (T + kRouteWaves - 1) / kRouteWaves;
+  hipLaunchKernelGGL(route_permute_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream, logits, bias, T,
+                     p->num_experts, p->n_group, p->topk_group, p->top_k, p->routed_scaling_factor,
+                     p->norm_topk_prob, ids, weights, nbits, offsets, sorted_slots, slot_rows, counter);
+  return launch_status("moe_route_permute");
 }
 
 }  // namespace moe

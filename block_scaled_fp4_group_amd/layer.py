@@ -19,8 +19,8 @@ from typing import Optional
 
 import torch
 
-from . import (MOE_ALGO_AUTO, Weights, combine, grouped_gemm, permute, permute_workspace_bytes, quantize_nvfp4,
-               route)
+from . import (MOE_ALGO_AUTO, Weights, combine, grouped_gemm, permute_workspace_bytes, quantize_nvfp4,
+               route_permute)
 
 
 @dataclasses.dataclass
@@ -52,6 +52,7 @@ class MoELayer:
         self.sorted_slots = torch.empty(R, dtype=i32, device=dev)
         self.slot_rows = torch.empty(R, dtype=i32, device=dev)
         self.ws = torch.empty(max(permute_workspace_bytes(T, top_k, E), 16), dtype=torch.uint8, device=dev)
+        self.counter = torch.zeros(1, dtype=i32, device=dev)   # router -> permutation hand-off (left zero)
         self.o = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
         self.y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         w4a4 = act_mode == "nvfp4"
@@ -77,8 +78,9 @@ class MoELayer:
                 events[name][i].record()
         R = T * self.top_k
         ids, topw = self.ids[:T], self.topw[:T]
-        route(logits, bias, self.E, self.n_group, self.topk_group, self.top_k, self.scale, True, ids=ids, weights=topw)
-        permute(ids, self.E, self.ws, self.offsets, self.sorted_slots[:R], self.slot_rows[:R])
+        route_permute(logits, bias, self.E, self.n_group, self.topk_group, self.top_k, self.scale, self.counter, True,
+                      ids=ids, weights=topw, workspace=self.ws, offsets=self.offsets,
+                      sorted_slots=self.sorted_slots[:R], slot_rows=self.slot_rows[:R])
         z = None if self.z is None else self.z[:R]
         o = self.o[:R]
         if self.act_mode == "nvfp4" and self.a_mode == "dequant":

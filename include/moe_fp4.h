@@ -101,6 +101,26 @@ moe_status moe_permute(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_
                        int32_t* expert_offsets, int32_t* sorted_slots, int32_t* slot_rows,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* --------------------------------------------------------- route + permute
+ * moe_route followed by moe_permute of the ids it wrote: the same outputs, bit
+ * for bit, as the two calls.  When T*top_k <= 2048 (every decode batch) both
+ * run in one launch: each router workgroup counts itself in *counter after
+ * writing its tokens' ids, and the last one to arrive runs the permutation,
+ * then sets *counter back to zero.  Larger batches make the two separate
+ * launches (workspace as for moe_permute; counter unused).
+ *   counter: one uint32 of device memory, 4-byte aligned, owned by the caller;
+ *            zero before the first call, and every call leaves it zero.  Calls
+ *            that share a counter must not run concurrently (same stream, or
+ *            ordered by events).
+ * Limits and errors as moe_route and moe_permute (E <= 256); NULL pointers and
+ * a misaligned counter give MOE_ERR_INVALID.
+ */
+moe_status moe_route_permute(const float* logits, const float* correction_bias, int64_t T,
+                             const moe_route_params* p, int32_t* topk_ids, float* topk_weights,
+                             int32_t* expert_offsets, int32_t* sorted_slots, int32_t* slot_rows,
+                             uint32_t* counter, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
 /* ----------------------------------------------------------- grouped GEMM
  * Per expert e and permuted row r in [expert_offsets[e], expert_offsets[e+1]):
  *   MOE_EPI_NONE:   out[r, n]  = sum_k A[r, k] * W0[e, n, k]

@@ -60,6 +60,26 @@ def test_permute_workspace_and_limits():
     _err(moe.lib.moe_permute(FAKE, 4, 8, 256, None, FAKE, FAKE, None, 0, None), moe.MOE_ERR_INVALID)
 
 
+def test_route_permute_rejects_bad_arguments():
+    def call(p, T=4, logits=FAKE, counter=FAKE, offsets=FAKE):
+        return moe.lib.moe_route_permute(logits, None, T, None if p is None else ctypes.byref(p), FAKE, FAKE,
+                                         offsets, FAKE, FAKE, counter, None, 0, None)
+    good = moe.RouteParams(256, 8, 4, 8, 2.827, 1)
+    for p in [moe.RouteParams(257, 8, 4, 8, 2.827, 1), moe.RouteParams(256, 7, 4, 8, 2.827, 1),
+              moe.RouteParams(256, 8, 4, 17, 2.827, 1), None]:
+        _err(call(p), moe.MOE_ERR_INVALID)
+    _err(call(good, counter=None), moe.MOE_ERR_INVALID)
+    _err(call(good, counter=ctypes.c_void_p(0x10002)), moe.MOE_ERR_INVALID)    # not 4-byte aligned
+    _err(call(good, logits=None), moe.MOE_ERR_INVALID)
+    _err(call(good, offsets=None), moe.MOE_ERR_INVALID)
+    _err(call(good, T=-1), moe.MOE_ERR_INVALID)
+    # above 2048 slots (two launches): pointers and the permutation workspace are checked before either launch
+    _err(moe.lib.moe_route_permute(None, None, 4096, ctypes.byref(good), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0,
+                                   None), moe.MOE_ERR_INVALID)
+    _err(moe.lib.moe_route_permute(FAKE, None, 4096, ctypes.byref(good), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 16,
+                                   None), moe.MOE_ERR_WORKSPACE)
+
+
 def _w(fmt=moe.MOE_FP4_MX, E=4, n=256, k=512, glob=None):
     return moe.Fp4Weights(fmt, E, n, k, 0x10000, 0x20000, glob)
 

@@ -126,6 +126,41 @@ def test_permute_parity(T, E, invalid):
     assert np.array_equal(host(sr), sr_ref)
 
 
+# --------------------------------------------------------- route + permute
+@pytest.mark.parametrize("T,E,n_group,topk_group,top_k,with_bias", [
+    (0, 256, 8, 4, 8, False), (1, 256, 8, 4, 8, False), (7, 256, 8, 4, 8, True), (64, 256, 8, 4, 8, True),
+    (255, 256, 8, 4, 8, False), (256, 256, 8, 4, 8, False), (300, 256, 8, 4, 8, True), (513, 64, 4, 2, 6, False),
+    (64, 16, 2, 1, 3, False)])
+def test_route_permute_parity(T, E, n_group, topk_group, top_k, with_bias):
+    """The fused call equals moe_route then moe_permute bit for bit (one launch
+    up to 2048 slots, two launches above), the oracle on its ids, and leaves the
+    hand-off counter at zero across calls."""
+    rng = np.random.default_rng(T * 31 + E)
+    counter = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for rep in range(3):
+        say(f"route_permute T={T} E={E} top_k={top_k} rep={rep}")
+        l = synth.random_logits(T * 7 + rep, T, E) if T else np.zeros((0, E), np.float32)
+        bias = (rng.standard_normal(E) * 0.1).astype(np.float32) if with_bias else None
+        db = None if bias is None else dev_f32(bias)
+        ids, wts, off, ss, sr = moe.route_permute(dev_f32(l), db, E, n_group, topk_group, top_k, 2.827, counter)
+        ids2, wts2 = moe.route(dev_f32(l), db, E, n_group, topk_group, top_k, 2.827)
+        off2, ss2, sr2 = moe.permute(ids2, E)
+        torch.cuda.synchronize()
+        assert int(host(counter)[0]) == 0
+        for a, b in ((ids, ids2), (wts, wts2), (off, off2), (ss, ss2), (sr, sr2)):
+            assert np.array_equal(host(a).view(np.int32), host(b).view(np.int32))
+        if T:
+            r = oracle.route(l, bias, n_group, topk_group, top_k, 2.827)
+            ok = ~r.near_tie
+            assert np.array_equal(host(ids)[ok], r.ids[ok])
+            off_ref, ss_ref, sr_ref = oracle.permute(host(ids), E)
+            assert np.array_equal(host(off), off_ref)
+            assert np.array_equal(host(ss), ss_ref)
+            assert np.array_equal(host(sr), sr_ref)
+        else:
+            assert np.array_equal(host(off), np.zeros(E + 1, np.int32))
+
+
 # --------------------------------------------------------------- quantise
 @pytest.mark.parametrize("g", [1.0, 0.5, 4.0])
 def test_quantize_nvfp4_parity(g):
