@@ -260,9 +260,10 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 // block routes its tokens, then adds one to *counter; the block that brings
 // it to gridDim.x has every block's ids behind it and runs the permutation,
 // then sets the counter back to zero for the next launch.  The fences are
-// device-scope release (each thread, after its stores) and acquire (the last
-// block, before its loads): the blocks sit on different XCDs, whose L2 caches
-// are not coherent with each other.
+// device-scope: a release by every wave after its own stores (before the block
+// counts itself in) and an acquire by the last block before its loads; the
+// other blocks skip the acquire and its cache invalidation.  The blocks sit on
+// different XCDs, whose L2 caches are not coherent with each other.
 __global__ __launch_bounds__(256) void route_permute_kernel(const float* __restrict__ logits,
                                                             const float* __restrict__ bias, int64_t T, int E,
                                                             int n_group, int topk_group, int top_k, float scale,
@@ -274,12 +275,12 @@ __global__ __launch_bounds__(256) void route_permute_kernel(const float* __restr
                                                             uint32_t* __restrict__ counter) {
   __shared__ int s_last;
   route_tokens(logits, bias, T, E, n_group, topk_group, top_k, scale, norm, ids, weights);
-  __threadfence();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // each wave, after its own stores
   __syncthreads();
   if (threadIdx.x == 0) s_last = atomicAdd(counter, 1u) == gridDim.x - 1;
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   permute_one_chunk(ids, T * top_k, E, nbits, offsets, sorted_slots, slot_rows);
   if (threadIdx.x == 0) atomicExch(counter, 0u);
 }
