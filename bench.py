@@ -8,9 +8,11 @@ resident in HBM.  The headline workload is the decode shape (256 experts in 8
 groups, keep 4 groups, top-8, hidden 4096, expert intermediate 2048, W4A16
 MXFP4) at a batch of 64 tokens; decode timings rotate four independent layer
 weight sets so the 256 MB Infinity Cache cannot serve repeated weight reads.
-The headline step is the layer replayed from a captured HIP graph (one graph
-per weight set); the eager step time is reported beside it, and the dominant
-kernel's time comes from HIP events around its launch in the eager steps.
+The headline step time comes from one captured HIP graph holding all K timed
+steps (each the layer on the next weight set, as successive layers of a decode
+step would be), replayed once; the eager step time is reported beside it, and
+the dominant kernel's time comes from HIP events around its launch in the
+eager steps.
 The JSON line also carries the batch-1/8 decode lines, the prefill, W4A4 and
 REAP-50 shapes, the roofline of the dominant kernel (the gate/up GEMM) and the
 CPU oracle timed on a bounded sample.
@@ -106,10 +108,13 @@ def time_steps(layers, inputs, steps, warmup, algo=0, ev_name="gate_up"):
 
 
 def graph_steps(layers, inputs, steps, warmup):
-    """The same steps as time_steps, each layer's forward captured once in a HIP
-    graph and replayed (inputs are the captured buffers).  Returns ms per step."""
+    """The same steps as time_steps captured in HIP graphs, as a decode engine
+    captures a whole token step: one graph of the warmup steps and one of the
+    timed steps, each step the layer forward of the next weight set in turn
+    (the rotating sets stand for successive layers).  Returns ms per step."""
     import torch
     x, l, b, r = inputs[0]
+    n = len(layers)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -117,21 +122,20 @@ def graph_steps(layers, inputs, steps, warmup):
             ly.forward(x, l, b, r)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    graphs = []
-    for ly in layers:
+
+    def capture(count):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            ly.forward(x, l, b, r)
-        graphs.append(g)
+            for i in range(count):
+                layers[i % n].forward(x, l, b, r)
+        return g
+    warm, timed = capture(max(warmup, 1)), capture(steps)
     torch.cuda.synchronize()
-    n = len(graphs)
-    for i in range(warmup):
-        graphs[i % n].replay()
+    warm.replay()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
-    for i in range(steps):
-        graphs[i % n].replay()
+    timed.replay()
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps
