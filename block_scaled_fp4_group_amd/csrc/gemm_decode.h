@@ -13,16 +13,17 @@
 // 16g..16g+15) reads one whole 32-value block (16 code bytes) of each of the 16
 // rows, dequantises it in registers (E2M1 x power-of-two scale -> bf16 with the
 // gfx950 convert instruction) and feeds four bf16 16x16x32 MFMAs whose other
-// operand holds 16 token rows.  Scales arrive as one 16-byte window per four
-// steps (MX) or two (NV).  For the model's K (4096, 2048) the step loop is
+// operand holds the pass's token rows (up to MR = 8 of its 16).  Scales
+// arrive as one 16-byte window per four steps (MX) or two (NV).  For the
+// model's K (4096, 2048) the step loop is
 // unrolled at compile time, so weight loads run PF steps ahead and token loads
 // PA steps ahead with every wait counted exactly; other K take a runtime loop.
 // For tiny batches KS waves split one tile's K range into contiguous pieces;
 // their partial sums meet in LDS in a fixed order (deterministic).  The
 // epilogue (SwiGLU, global scales, bf16 and/or NVFP4 output) runs on the
-// accumulator registers.  More than 16 token rows of one expert take further
-// passes over the same weights (served from L2).  Token rows past the
-// expert's end read a valid row; their output columns are never stored.
+// accumulator registers.  An expert with more than MR token rows takes
+// further passes over the same weights (served from L2).  Token rows past the
+// pass's end read a valid row; their output columns are never stored.
 #pragma once
 #include <algorithm>
 
