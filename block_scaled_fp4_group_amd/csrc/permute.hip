@@ -50,6 +50,11 @@ __global__ __launch_bounds__(kPermThreads) void permute_count(const int32_t* __r
   for (int e = threadIdx.x; e < E; e += kPermThreads) table[(int64_t)blockIdx.x * E + e] = hist[e];
 }
 
+// The [nblk, E] count table is read twice, kScanBatch blocks at a time with
+// every load of a batch in flight together: once to total each expert, once
+// (after the scan over experts) to write each (block, expert) base row.
+constexpr int kScanBatch = 16;
+
 __global__ __launch_bounds__(kPermThreads) void permute_scan(int32_t* __restrict__ table, int nblk, int E,
                                                              int32_t* __restrict__ offsets) {
   __shared__ int32_t tot[kPermMaxE];
@@ -57,10 +62,12 @@ __global__ __launch_bounds__(kPermThreads) void permute_scan(int32_t* __restrict
   __shared__ int32_t range_total;
   for (int e = threadIdx.x; e < E; e += kPermThreads) {
     int32_t run = 0;
-    for (int b = 0; b < nblk; ++b) {
-      int32_t c = table[(int64_t)b * E + e];
-      table[(int64_t)b * E + e] = run;
-      run += c;
+    for (int b0 = 0; b0 < nblk; b0 += kScanBatch) {
+      int32_t c[kScanBatch];
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u) c[u] = table[(int64_t)min(b0 + u, nblk - 1) * E + e];
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u) run += b0 + u < nblk ? c[u] : 0;
     }
     tot[e] = run;
   }
@@ -80,8 +87,19 @@ __global__ __launch_bounds__(kPermThreads) void permute_scan(int32_t* __restrict
   if (threadIdx.x == 0) offsets[E] = carry;
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kPermThreads) {
-    int32_t b0 = tot[e];
-    for (int b = 0; b < nblk; ++b) table[(int64_t)b * E + e] += b0;
+    int32_t run = tot[e];
+    for (int b0 = 0; b0 < nblk; b0 += kScanBatch) {
+      int32_t c[kScanBatch];
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u) c[u] = table[(int64_t)min(b0 + u, nblk - 1) * E + e];
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u) {
+        if (b0 + u < nblk) {
+          table[(int64_t)(b0 + u) * E + e] = run;
+          run += c[u];
+        }
+      }
+    }
   }
 }
 
