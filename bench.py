@@ -200,7 +200,7 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for {args.gpus}).",
+        print(f"bench.py runs on one GPU only: the library has no multi-GPU path (asked for {args.gpus}).",
               file=sys.stderr, flush=True)
         sys.exit(2)
 
