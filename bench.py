@@ -159,18 +159,35 @@ def layer_bytes(D, T, shape):
     return D * 3 * I * H * MX_BYTES_PER_WEIGHT + T * (2 * H + 4 * E + 64 + 2 * H)
 
 
-def cpu_baseline(shape, W, x, l, bias, sample_tokens):
-    import oracle
+def cpu_model():
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(shape, W, x, l, bias, sample_tokens):
+    """The oracle on a bounded sample, with NumPy's BLAS pool set to the cores
+    this process may run on.  Returns (tokens/s, seconds, threads used, cores)."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limiter = threadpool_limits(limits=cores, user_api="blas")
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
-        threads = 1
+        limiter, threads = None, 1
     t0 = time.perf_counter()
     oracle.moe_layer(x, l, bias, W, shape.n_group, shape.topk_group, shape.top_k, shape.routed_scaling_factor,
                      tokens=sample_tokens)
     dt = time.perf_counter() - t0
-    return len(sample_tokens) / dt, dt, threads
+    if limiter is not None:
+        limiter.restore_original_limits()
+    return len(sample_tokens) / dt, dt, threads, cores
 
 
 def main():
@@ -286,10 +303,12 @@ def main():
     if not args.no_cpu:
         log("[bench] CPU oracle baseline")
         sample = list(range(12))          # about 10 s of float64 work on the host
-        v, dt, threads = cpu_baseline(s, Ws[0], main_r["x"], main_r["l"], None, sample)
+        v, dt, threads, cores = cpu_baseline(s, Ws[0], main_r["x"], main_r["l"], None, sample)
         out["cpu_baseline"] = {"value": round(v, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                               "cpu": cpu_model(), "cores_available": cores,
                                "sample": f"oracle.moe_layer on the decode T=64 batch: routing and permutation of all 64 "
-                                         f"tokens, expert FFNs and combine of tokens {sample} (float64 NumPy), "
+                                         f"tokens, expert FFNs and combine of tokens {sample} (float64 NumPy, "
+                                         f"BLAS threads {threads} of {cores} cores in the affinity mask), "
                                          f"{dt:.1f} s wall"}
     print(json.dumps(out), flush=True)
 

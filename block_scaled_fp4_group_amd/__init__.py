@@ -21,7 +21,7 @@ MOE_FP4_MX, MOE_FP4_NV = 0, 1
 MOE_FP4_SCALES_POW2, MOE_FP4_TILED = 1, 2
 MOE_ACT_BF16, MOE_ACT_NVFP4 = 0, 1
 MOE_EPI_NONE, MOE_EPI_SWIGLU = 0, 1
-MOE_ALGO_AUTO, MOE_ALGO_DECODE, MOE_ALGO_PREFILL, MOE_ALGO_DECODE_PERSISTENT = 0, 1, 2, 3
+MOE_ALGO_AUTO, MOE_ALGO_DECODE, MOE_ALGO_PREFILL = 0, 1, 2
 
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_version", "moe_route", "moe_permute_workspace_bytes",
            "moe_permute", "moe_route_permute", "moe_fp4_grouped_gemm", "moe_combine", "fp4_transcode_mx_to_nv", "moe_quantize_nvfp4",

@@ -35,7 +35,7 @@ moe_status launch_combine(const void*, const int32_t*, const float*, const void*
 moe_status launch_transcode(const uint8_t*, const uint8_t*, int64_t, int, int, uint8_t*, float*, int64_t*, hipStream_t);
 moe_status launch_quant(const void*, int64_t, int, float, uint8_t*, uint8_t*, void*, hipStream_t);
 moe_status launch_tile(bool, int64_t, int, int, const uint8_t*, const uint8_t*, uint8_t*, uint8_t*, hipStream_t);
-moe_status launch_gemm_decode(const GemmArgs&, bool swiglu, int wf, bool a_nv, int64_t rows, int persistent, hipStream_t);
+moe_status launch_gemm_decode(const GemmArgs&, bool swiglu, int wf, bool a_nv, int64_t rows, hipStream_t);
 moe_status launch_gemm_prefill(const GemmArgs&, bool swiglu, int wf, bool a_nv, int64_t rows, hipStream_t);
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -208,7 +208,7 @@ moe_status moe_fp4_grouped_gemm(const moe_act* a, const moe_fp4_weights* w0, con
   if (out->codes) MOE_CHECK(out->scales != nullptr, "moe_fp4_grouped_gemm: NVFP4 output needs scales");
   if (out->codes || out->dequant)
     MOE_CHECK(is_pow2_float(out->output_scale), "moe_fp4_grouped_gemm: output_scale must be a power of two");
-  MOE_CHECK(algo >= MOE_ALGO_AUTO && algo <= MOE_ALGO_DECODE_PERSISTENT, "moe_fp4_grouped_gemm: bad algo");
+  MOE_CHECK(algo >= MOE_ALGO_AUTO && algo <= MOE_ALGO_PREFILL, "moe_fp4_grouped_gemm: bad algo");
   if (rows == 0) return MOE_OK;
 
   GemmArgs g;
@@ -247,7 +247,7 @@ moe_status moe_fp4_grouped_gemm(const moe_act* a, const moe_fp4_weights* w0, con
   int use = algo;
   if (use == MOE_ALGO_AUTO) use = (rows >= 32LL * g.E) ? MOE_ALGO_PREFILL : MOE_ALGO_DECODE;
   if (use == MOE_ALGO_PREFILL) return launch_gemm_prefill(g, swiglu, wf, a_nv, rows, stream);
-  return launch_gemm_decode(g, swiglu, wf, a_nv, rows, use == MOE_ALGO_DECODE_PERSISTENT, stream);
+  return launch_gemm_decode(g, swiglu, wf, a_nv, rows, stream);
 }
 
 moe_status moe_combine(const void* expert_out, const int32_t* slot_rows, const float* topk_weights,

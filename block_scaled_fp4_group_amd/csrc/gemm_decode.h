@@ -278,37 +278,25 @@ __device__ __forceinline__ void stage_rows(const GemmArgs& p, uint8_t* lds, int 
   }
 }
 
-// Tuning: token rows per pass (LDS holds MR rows of K bf16) and weight steps in
-// flight per wave (the LDS stage caps occupancy, so deep register rings are free).
-#ifndef MOE_DEC_MR_4096
-#define MOE_DEC_MR_4096 8
-#endif
-#ifndef MOE_DEC_MR_2048
-#define MOE_DEC_MR_2048 8
-#endif
-#ifndef MOE_DEC_PF2
-#define MOE_DEC_PF2 8
-#endif
-#ifndef MOE_DEC_PF1
-#define MOE_DEC_PF1 4
-#endif
-#ifndef MOE_DEC_NT2
-#define MOE_DEC_NT2 2          // 16-row tiles per wave, gate/up
-#endif
-#ifndef MOE_DEC_NWN1
-#define MOE_DEC_NWN1 8         // waves per workgroup when many waves stream: one matrix (down)
-#endif
-#ifndef MOE_DEC_NWN2
-#define MOE_DEC_NWN2 4         // ... gate/up
-#endif
-__host__ __device__ constexpr int decode_rows_per_pass(int K) { return K > 2048 ? MOE_DEC_MR_4096 : MOE_DEC_MR_2048; }
+// Token rows per pass (LDS holds kDecRows rows of K bf16), weight steps in
+// flight per wave (the LDS stage caps occupancy, so deep register rings are
+// free), 16-row tiles per gate/up wave, and waves per workgroup when many waves
+// stream (measured best of 4, 8 and 16 waves; 4 / 8 / 16 rows per pass; 1 or 2
+// tiles per wave).
+constexpr int kDecRows = 8;
+constexpr int kDecRing2 = 8;           // gate/up (two matrices)
+constexpr int kDecRing1 = 4;           // down
+constexpr int kDecTiles2 = 2;
+constexpr int kDecWaves1 = 8;          // down
+constexpr int kDecWaves2 = 4;          // gate/up
+__host__ __device__ constexpr int decode_rows_per_pass(int) { return kDecRows; }
 __host__ __device__ constexpr int decode_pitch(int K) { return K * 2 + 16; }
 
 template <int NMAT, int NWN, int KS, int NT, int NS, int WF, bool A_NV, bool TL>
 __global__ __launch_bounds__(NWN * KS * 64) void gemm_decode_kernel(GemmArgs p) {
   constexpr bool W_NV = WF != 0;
   // the general NVFP4 conversion needs more registers: a shorter weight ring
-  constexpr int PF = NMAT == 2 ? (WF == 2 ? 4 : MOE_DEC_PF2) : MOE_DEC_PF1, PA = 2;
+  constexpr int PF = NMAT == 2 ? (WF == 2 ? 4 : kDecRing2) : kDecRing1, PA = 2;
   static_assert(KS == 1 || NT == 1, "the K split runs one tile per wave");
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int wn = wv % NWN, ks = wv / NWN;
@@ -395,194 +383,6 @@ __global__ __launch_bounds__(NWN * KS * 64) void gemm_decode_kernel(GemmArgs p) 
   }
 }
 
-// ------------------------------------------------------------- persistent
-// The same weight streaming for batches that keep every CU busy, without the
-// start-up and drain of a workgroup per (expert, n-block): persistent
-// workgroups of 8 waves (one per CU at K = 4096, two at K = 2048) each walk a
-// contiguous slice of one work list.
-//   * a segment is up to MR token rows of one expert (an expert with more rows
-//     has several, in row order); a unit is one 16-row weight tile (one per
-//     matrix) of one segment; the list holds every (segment, tile) in order;
-//   * wave w of a workgroup takes units w, w + 8, w + 16, ... of the slice, and
-//     its weight pipeline runs on across them: the last steps of a unit load
-//     the first steps of the next one (the wave's last unit reloads its own
-//     recent steps instead, which L2 still holds);
-//   * token rows sit in two LDS stages, segment s in stage s % 2.  Eight
-//     consecutive units touch at most two segments (a segment has >= 8 units),
-//     so a segment is staged by the whole workgroup, between two barriers, at
-//     the start of the first round of 8 units that needs it; the stage it
-//     overwrites belongs to a segment the previous rounds finished.
-constexpr int kPsWaves = 8;
-constexpr int kPsMaxSeg = 1536;
-// workgroups per CU: the two row stages of K = 4096 fill LDS; those of K = 2048
-// leave room for a second workgroup of one matrix (16 waves stream per CU, in
-// 128 registers each; the SwiGLU pair needs more)
-constexpr int persist_wg_per_cu(int nmat, int ns) { return (ns >= 32 || nmat == 2) ? 1 : 2; }
-
-template <int NMAT, int NS, int WF, bool A_NV, bool TL>
-__global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(2 * persist_wg_per_cu(NMAT, NS))))
-void gemm_decode_persist_kernel(GemmArgs p) {
-  constexpr bool W_NV = WF != 0;
-  // 8 weight steps in flight per wave (the general NVFP4 conversion needs the
-  // registers of half of them)
-  constexpr int PF = (NMAT == 2 && WF == 2) ? 4 : 8, PA = 2;
-  constexpr int SWN = DecodeWave<NMAT, WF, TL>::SWN;
-  using WL = WeightLane<TL, W_NV>;
-  static_assert(NS % PF == 0 && NS % 16 == 0, "whole weight and scale-window rings per unit");
-  extern __shared__ __attribute__((aligned(16))) uint8_t a_lds[];   // two token-row stages
-  __shared__ int s_e[kPsMaxSeg], s_r0[kPsMaxSeg];
-  __shared__ uint8_t s_m[kPsMaxSeg];
-  __shared__ int s_wc[kPsWaves];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int li = lane & 15, lg = lane >> 4;
-  const int K = p.K, N = p.N;
-  const int MR = decode_rows_per_pass(K), pitch = decode_pitch(K);
-  const int stage_bytes = MR * pitch;
-  const int ups = N / 16;                                     // units per segment
-
-  // segment table: expert e's rows [r0, r1) cut into passes of MR rows
-  int nseg = 0;
-  for (int e0 = 0; e0 < p.E; e0 += kPsWaves * 64) {
-    const int e = e0 + tid;
-    int r0 = 0, r1 = 0;
-    if (e < p.E) {
-      r0 = (int)max((int64_t)0, min((int64_t)p.offsets[e], p.rows));
-      r1 = (int)max((int64_t)r0, min((int64_t)p.offsets[e + 1], p.rows));
-    }
-    const int cnt = (r1 - r0 + MR - 1) / MR;
-    int x = cnt;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(x, off, kWave);
-      if (lane >= off) x += y;
-    }
-    if (lane == 63) s_wc[wv] = x;
-    __syncthreads();
-    int s = nseg + x - cnt;
-    for (int i = 0; i < wv; ++i) s += s_wc[i];
-    for (int q = 0; q < cnt && s < kPsMaxSeg; ++q, ++s) {    // (only malformed offsets reach the cap)
-      s_e[s] = e;
-      s_r0[s] = r0 + q * MR;
-      s_m[s] = (uint8_t)min(MR, r1 - r0 - q * MR);
-    }
-    for (int i = 0; i < kPsWaves; ++i) nseg += s_wc[i];
-    __syncthreads();
-  }
-  nseg = min(nseg, kPsMaxSeg);
-
-  // this workgroup's slice [lo, hi) of the units; this wave's units u0, u0 + 8, ..
-  const int64_t total = (int64_t)nseg * ups;
-  const int lo = (int)(total * blockIdx.x / gridDim.x), hi = (int)(total * (blockIdx.x + 1) / gridDim.x);
-  const int rounds = (hi - lo + kPsWaves - 1) / kPsWaves;
-  const int u0 = lo + wv;
-  const int nmine = u0 < hi ? (hi - u0 + kPsWaves - 1) / kPsWaves : 0;
-  const int ulast = u0 + (nmine - 1) * kPsWaves;
-
-  // one buffer resource per matrix over all experts (< 4 GiB, checked on the
-  // host); a unit's base goes in the scalar offset
-  const uint32_t sc_row = (uint32_t)(W_NV ? K / 16 : K / 32);
-  const uint32_t mat_codes = (uint32_t)N * (uint32_t)(K / 2);
-  const uint32_t mat_scales = (uint32_t)N * sc_row;
-  rsrc_t wr_[NMAT], sr_[NMAT];
-#pragma unroll
-  for (int m = 0; m < NMAT; ++m) {
-    wr_[m] = make_rsrc(p.w_packed[m], (uint32_t)((uint64_t)p.E * mat_codes));
-    sr_[m] = make_rsrc(p.w_scale[m], (uint32_t)((uint64_t)p.E * mat_scales));
-  }
-  const uint32_t vo_w = WL::code(li, lg, K);                 // row li, block lg of a step
-  const uint32_t vo_s = WL::scale(li, K);
-  auto unit_base = [&](int u, uint32_t& bw, uint32_t& bs) {
-    const int seg = u / ups, tile = u - seg * ups;
-    const uint32_t e = (uint32_t)__builtin_amdgcn_readfirstlane(s_e[seg]);
-    bw = e * mat_codes + (uint32_t)tile * 16u * (uint32_t)(K / 2);
-    bs = e * mat_scales + (uint32_t)tile * 16u * sc_row;
-  };
-  auto wload = [&](WStage<NMAT>& S, uint32_t bw, int i) {
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m) S.w[m] = bload128(wr_[m], vo_w + (uint32_t)i * WL::kStep, bw);
-  };
-  // scale window c (steps 4c .. 4c+3) of a unit: MX 16 B, NV 32 B per row
-  auto sload = [&](u32x4 (&W)[NMAT][SWN], uint32_t bs, int c) {
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-      for (int h = 0; h < SWN; ++h) W[m][h] = bload128(sr_[m], vo_s + (uint32_t)c * WL::kWin + 16u * h, bs);
-  };
-
-  DecodeWave<NMAT, WF, TL> dw;
-  dw.lg = lg;
-  WStage<NMAT> wr[PF];
-  AStage ar[PA];
-  // scale windows two super-steps ahead (4-entry ring): loads complete in
-  // order, so a window due sooner would cut the weight ring's depth
-  u32x4 sw[4][NMAT][SWN];
-  uint32_t cw = 0, cs = 0;                                    // current unit's bases
-  if (nmine > 0) {
-    unit_base(u0, cw, cs);
-    sload(sw[0], cs, 0);
-    sload(sw[1], cs, 1);
-#pragma unroll
-    for (int q = 0; q < PF; ++q) wload(wr[q], cw, q);         // weights in flight while the rows stage
-  }
-
-  int staged = -1;                                            // highest segment staged so far
-  int u = u0;
-  for (int k = 0; k < rounds; ++k, u += kPsWaves) {
-    const int ra = lo + k * kPsWaves, rb = min(ra + kPsWaves, hi) - 1;
-    const int s_hi = rb / ups;
-    if (s_hi > staged) {                                      // uniform over the workgroup
-      if (k > 0) __syncthreads();                             // every wave done with the previous rounds
-      for (int s = max(staged + 1, ra / ups); s <= s_hi; ++s)
-        stage_rows<A_NV>(p, a_lds + (s & 1) * stage_bytes, s_r0[s], s_m[s], pitch);
-      staged = s_hi;
-      __syncthreads();
-    }
-    if (u >= hi) continue;                                    // (last round only)
-    const int seg = u / ups;
-    const int mrows = s_m[seg], rbase = s_r0[seg];
-    const bool arow_ok = li < mrows;
-    // rows >= mrows read row 0 of the stage; their output columns are dropped
-    dw.al = a_lds + (seg & 1) * stage_bytes + (arow_ok ? li : 0) * pitch + lg * 64;
-    const int e = __builtin_amdgcn_readfirstlane(s_e[seg]);
-    float wglob[NMAT];
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m) wglob[m] = W_NV ? p.w_global[m][e] : 1.0f;
-    uint32_t nw, ns;                                          // next unit's bases
-    if (u < ulast) {
-      unit_base(u + kPsWaves, nw, ns);
-    } else {                                                  // the loads below then repeat this unit's last steps
-      nw = cw + (uint32_t)(NS - PF) * WL::kStep;
-      ns = cs + (uint32_t)(NS / 4 - 2) * WL::kWin;
-    }
-#pragma unroll
-    for (int q = 0; q < PA; ++q) dw.aload(ar[q], q);
-    dw.clear();
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const int cg = i / 4, j = i % 4;
-      if (j == 0) {                                           // window cg + 2 (of the next unit past the end)
-        if ((cg + 2) * 4 < NS) sload(sw[(cg + 2) & 3], cs, cg + 2);
-        else sload(sw[(cg + 2) & 3], ns, cg + 2 - NS / 4);
-      }
-      uint32_t sb[NMAT];
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m) sb[m] = dw.sbits(sw[cg & 3][m], j);
-      dw.consume(wr[i % PF], ar[i % PA], sb);
-      if (i + PA < NS) dw.aload(ar[i % PA], i + PA);
-      if (i + PF < NS) wload(wr[i % PF], cw, i + PF);
-      else wload(wr[i % PF], nw, i + PF - NS);
-      // keep this step's loads here: the scheduler would otherwise sink them
-      // next to their use and shrink the ring to a step or two in flight
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    decode_finish<NMAT>(p, dw.acc, wglob, rbase + li, arow_ok, (u - seg * ups) * 16, lg);
-    cw = nw;
-    cs = ns;
-  }
-}
-
 template <int NMAT, int NWN, int KS, int NT, int NS, int WF, bool A_NV, bool TL>
 static void launch_decode_one(const GemmArgs& a, int nact, hipStream_t stream) {
   auto kern = gemm_decode_kernel<NMAT, NWN, KS, NT, NS, WF, A_NV, TL>;
@@ -614,7 +414,7 @@ static void launch_decode_t(const GemmArgs& a, int wf, bool a_nv, int nact, hipS
 template <bool TL, int NMAT, int NWN, int KS>
 static void launch_decode_k(const GemmArgs& a, int wf, bool a_nv, int nact, hipStream_t stream) {
   const int nsteps = a.K / 128;
-  constexpr int NT = (KS > 1 || NMAT == 1) ? 1 : MOE_DEC_NT2;
+  constexpr int NT = (KS > 1 || NMAT == 1) ? 1 : kDecTiles2;
   if (KS == 1 && a.N % (16 * NWN * NT) == 0) {
     if (nsteps == 32) return launch_decode_t<TL, NMAT, NWN, KS, NT, 32>(a, wf, a_nv, nact, stream);
     if (nsteps == 16) return launch_decode_t<TL, NMAT, NWN, KS, NT, 16>(a, wf, a_nv, nact, stream);
@@ -633,7 +433,7 @@ static void launch_decode_ks(const GemmArgs& a, int wf, bool a_nv, int nact, hip
   if (a.N % 64 != 0) {
     launch_decode_k<TL, NMAT, 1, 1>(a, wf, a_nv, nact, stream);
   } else if (waves >= 2048 || nsteps % 8 != 0) {
-    constexpr int NWN = NMAT == 1 ? MOE_DEC_NWN1 : MOE_DEC_NWN2;
+    constexpr int NWN = NMAT == 1 ? kDecWaves1 : kDecWaves2;
     if (a.N % (16 * NWN) == 0) launch_decode_k<TL, NMAT, NWN, 1>(a, wf, a_nv, nact, stream);
     else launch_decode_k<TL, NMAT, 4, 1>(a, wf, a_nv, nact, stream);
   } else if (waves >= 1024 || nsteps % 16 != 0) {
@@ -641,49 +441,6 @@ static void launch_decode_ks(const GemmArgs& a, int wf, bool a_nv, int nact, hip
   } else {
     launch_decode_k<TL, NMAT, 1, 4>(a, wf, a_nv, nact, stream);
   }
-}
-
-#ifndef MOE_DEC_PERSIST
-#define MOE_DEC_PERSIST 0      // persistent kernel by batch size (measured slower at 64 tokens: off)
-#endif
-#ifndef MOE_DEC_PERSIST_MIN
-#define MOE_DEC_PERSIST_MIN 2  // ... with at least this many units per wave
-#endif
-
-template <int NMAT, int NS, int WF, bool A_NV, bool TL>
-static void launch_persist_one(const GemmArgs& a, hipStream_t stream) {
-  auto kern = gemm_decode_persist_kernel<NMAT, NS, WF, A_NV, TL>;
-  const size_t lds = 2 * (size_t)decode_rows_per_pass(a.K) * decode_pitch(a.K);   // NS fixes K
-  static bool attr_set = false;               // one-time opt-in to > 64 KB of LDS
-  if (!attr_set) {
-    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(kern, dim3(device_cus() * persist_wg_per_cu(NMAT, NS)), dim3(kPsWaves * 64), lds, stream, a);
-}
-
-template <bool TL, int NMAT, int NS>
-static void launch_persist_t(const GemmArgs& a, int wf, bool a_nv, hipStream_t stream) {
-  switch (wf) {
-    case 0: a_nv ? launch_persist_one<NMAT, NS, 0, true, TL>(a, stream) : launch_persist_one<NMAT, NS, 0, false, TL>(a, stream); break;
-    case 1: a_nv ? launch_persist_one<NMAT, NS, 1, true, TL>(a, stream) : launch_persist_one<NMAT, NS, 1, false, TL>(a, stream); break;
-    default: a_nv ? launch_persist_one<NMAT, NS, 2, true, TL>(a, stream) : launch_persist_one<NMAT, NS, 2, false, TL>(a, stream); break;
-  }
-}
-
-// The persistent kernel covers the model's K (4096, 2048), N >= 128 in whole
-// tiles, weights of one matrix set under 4 GiB, a segment table that cannot
-// overflow for well-formed offsets, and batches with enough units per wave.
-inline bool persist_fits(const GemmArgs& a, bool swiglu, int64_t rows, int nact, bool force) {
-  if (!MOE_DEC_PERSIST && !force) return false;
-  const int nsteps = a.K / 128;
-  if (a.K % 128 != 0 || (nsteps != 32 && nsteps != 16)) return false;
-  if (a.N % 16 != 0 || a.N / 16 < kPsWaves) return false;
-  const int mr = decode_rows_per_pass(a.K);
-  if ((rows + (int64_t)nact * (mr - 1)) / mr > kPsMaxSeg) return false;
-  if ((uint64_t)a.E * (uint64_t)a.N * (uint64_t)(a.K / 2) > 0xFFFFFFFFull) return false;
-  const int64_t waves = (int64_t)device_cus() * persist_wg_per_cu(swiglu ? 2 : 1, nsteps) * kPsWaves;
-  return force || (int64_t)nact * (a.N / 16) >= waves * MOE_DEC_PERSIST_MIN;
 }
 
 // Launchers of one weight layout (TL: tiled), each instantiated in its own
@@ -694,16 +451,7 @@ void decode_wg(const GemmArgs& a, bool swiglu, int wf, bool a_nv, int nact, hipS
   else launch_decode_ks<TL, 1>(a, wf, a_nv, nact, stream);
 }
 
-template <bool TL>
-void decode_persist(const GemmArgs& a, bool swiglu, int wf, bool a_nv, hipStream_t stream) {
-  const bool k4096 = a.K / 128 == 32;
-  if (swiglu) k4096 ? launch_persist_t<TL, 2, 32>(a, wf, a_nv, stream) : launch_persist_t<TL, 2, 16>(a, wf, a_nv, stream);
-  else k4096 ? launch_persist_t<TL, 1, 32>(a, wf, a_nv, stream) : launch_persist_t<TL, 1, 16>(a, wf, a_nv, stream);
-}
-
 extern template void decode_wg<false>(const GemmArgs&, bool, int, bool, int, hipStream_t);
 extern template void decode_wg<true>(const GemmArgs&, bool, int, bool, int, hipStream_t);
-extern template void decode_persist<false>(const GemmArgs&, bool, int, bool, hipStream_t);
-extern template void decode_persist<true>(const GemmArgs&, bool, int, bool, hipStream_t);
 
 }  // namespace moe

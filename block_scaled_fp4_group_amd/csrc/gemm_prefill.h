@@ -303,11 +303,9 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& p, const PfTile& T, 
 }
 
 // ------------------------------------------------ bf16 tokens: direct to LDS
-#ifndef MOE_PF_WREG
-#define MOE_PF_WREG 1          // 64 x 512 tiles: weight codes in registers, not LDS (3-4%
-                               // faster, although the compiler then drains the loads in
-                               // flight once per step before the first LDS read)
-#endif
+// 64 x 512 tiles: weight codes in registers, not LDS (3-4% faster, although the
+// compiler then drains the loads in flight once per step before the first LDS read)
+constexpr bool kPfWeightRegs = true;
 template <int S>
 __device__ __forceinline__ uint8_t* pf_stage() {
   return S == 0 ? pf_stage0 : (S == 1 ? pf_stage1 : pf_stage2);
@@ -324,7 +322,7 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_dma_kernel(GemmArgs p
   // 64 x 512: every weight row belongs to one wave, so its codes go straight
   // into that wave's registers (4 loads of 16 B per lane and step, three steps
   // deep) instead of through LDS
-  constexpr bool WREG = MOE_PF_WREG && SH::BM == 64;
+  constexpr bool WREG = kPfWeightRegs && SH::BM == 64;
   using WL = WeightLane<TL, W_NV>;
   constexpr int kA = SH::BM / 32, kW = WREG ? 4 : SH::BN / 128;
   constexpr int kSRows = W_NV ? 32 : 64;                              // weight rows per scale load
@@ -622,9 +620,6 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_nv_kernel(GemmArgs p)
 }
 
 // ------------------------------------------------------------------- host
-#ifndef MOE_PF_WIDE
-#define MOE_PF_WIDE 1          // bf16 tokens: 64 x 512 tiles where N allows
-#endif
 template <int NMAT, int WF, bool A_NV, bool TL>
 static void launch_prefill_one(const GemmArgs& a, hipStream_t stream) {
   // persistent: one workgroup per CU (8 waves); tiles are distributed on the device
@@ -636,7 +631,7 @@ static void launch_prefill_one(const GemmArgs& a, hipStream_t stream) {
       attr_set = true;
     }
     hipLaunchKernelGGL(kern, dim3(device_cus()), dim3(kPfThreads), 2 * PfTall::Stage, stream, a);
-  } else if (a.N % (PfWide::BN / NMAT) == 0 && MOE_PF_WIDE) {
+  } else if (a.N % (PfWide::BN / NMAT) == 0) {      // bf16 tokens: 64 x 512 tiles where N allows
     hipLaunchKernelGGL((gemm_prefill_dma_kernel<NMAT, WF, TL, PfWide>), dim3(device_cus()), dim3(kPfThreads), 0, stream, a);
   } else {
     hipLaunchKernelGGL((gemm_prefill_dma_kernel<NMAT, WF, TL, PfTall>), dim3(device_cus()), dim3(kPfThreads), 0, stream, a);

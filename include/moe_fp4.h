@@ -203,18 +203,24 @@ typedef struct {
 #define MOE_ALGO_DECODE 1     /* weight-streaming kernel (few rows per expert): one
                                  workgroup per (expert, block of output features)         */
 #define MOE_ALGO_PREFILL 2    /* LDS-tiled MFMA kernel (many rows per expert)             */
-#define MOE_ALGO_DECODE_PERSISTENT 3  /* weight streaming by persistent workgroups that walk
-                                 one work list (k 4096 or 2048, n >= 128; other shapes
-                                 run as MOE_ALGO_DECODE)                                  */
 
 moe_status moe_fp4_grouped_gemm(const moe_act* a, const moe_fp4_weights* w0, const moe_fp4_weights* w1,
                                 moe_epilogue epi, const int32_t* expert_offsets, int64_t rows,
                                 const moe_out* out, int32_t algo, hipStream_t stream);
 
 /* ---------------------------------------------------------------- combine
+ * The layer output of each token is the sum of its routed experts' outputs,
+ * each weighted by the router's gate value g_{t,j} for that expert (the REAP
+ * saliency equation on the "MiMo-V2.6-Flash -- REAP-50" card, "Pruning
+ * Method", weighs every expert output of token t by g_{t,j}); the residual
+ * stream is added in the same pass:
  * y[t, :] = bf16( residual[t, :] + sum_{j=0..top_k-1} w[t, j] * expert_out[slot_rows[t*top_k+j], :] )
  * summed in FP32 in j order (residual may be NULL; slot_rows = -1 contributes 0).
- *   expert_out bf16 [R, h]; topk_weights float [T, top_k]; y bf16 [T, h]; h % 8 == 0.
+ *   expert_out bf16 [R, h]; slot_rows int32 [T*top_k] (moe_permute's inverse map);
+ *   topk_weights float [T, top_k]; residual bf16 [T, h] or NULL; y bf16 [T, h].
+ *   h % 8 == 0, 1 <= top_k <= 32; bf16 buffers 16-byte aligned.  T == 0 is a no-op.
+ * Errors: MOE_ERR_INVALID for a NULL pointer, bad sizes or misalignment (nothing
+ * is written); a slot_rows entry outside [-1, R) is the caller's error (unchecked).
  */
 moe_status moe_combine(const void* expert_out, const int32_t* slot_rows, const float* topk_weights,
                        const void* residual, int64_t T, int32_t top_k, int32_t h, void* y,

@@ -56,12 +56,18 @@ def down_proj(z_bits: np.ndarray, wd: np.ndarray, act_mode: str = "bf16", input_
     return _act_values(z_bits, act_mode, input_scale) @ wd.T
 
 
-def combine(o: np.ndarray, weights: np.ndarray, residual_bits: Optional[np.ndarray] = None) -> np.ndarray:
-    """o float64 [T, top_k, H], weights [T, top_k] -> y bf16 bits [T, H]."""
+def combine_f64(o: np.ndarray, weights: np.ndarray, residual_bits: Optional[np.ndarray] = None) -> np.ndarray:
+    """o float64 [T, top_k, H], weights [T, top_k] -> the layer output in
+    float64 [T, H], before its one rounding to bfloat16."""
     acc = np.zeros((o.shape[0], o.shape[2])) if residual_bits is None else bf16_value(residual_bits).copy()
     for j in range(o.shape[1]):
         acc = acc + weights[:, j:j + 1] * o[:, j, :]
-    return round_to_bf16_bits(acc)
+    return acc
+
+
+def combine(o: np.ndarray, weights: np.ndarray, residual_bits: Optional[np.ndarray] = None) -> np.ndarray:
+    """o float64 [T, top_k, H], weights [T, top_k] -> y bf16 bits [T, H]."""
+    return round_to_bf16_bits(combine_f64(o, weights, residual_bits))
 
 
 def dequant_expert(weights: dict, e: int, fmt: str):
@@ -88,6 +94,7 @@ class LayerResult:
     z: np.ndarray                    # bf16 bits [len(tokens), top_k, I]
     o: np.ndarray                    # float64 [len(tokens), top_k, H]
     y: np.ndarray                    # bf16 bits [len(tokens), H]
+    y_f64: np.ndarray                # float64 [len(tokens), H]: y before its bf16 rounding
 
 
 def moe_layer(x_bits: np.ndarray, logits: np.ndarray, bias: Optional[np.ndarray], weights: dict,
@@ -119,6 +126,7 @@ def moe_layer(x_bits: np.ndarray, logits: np.ndarray, bias: Optional[np.ndarray]
         z[where[:, 0], where[:, 1]] = ze
         o[where[:, 0], where[:, 1]] = oe
     res = None if residual_bits is None else residual_bits[toks]
-    y = combine(o, r.weights[toks], res)
+    y_f64 = combine_f64(o, r.weights[toks], res)
     return LayerResult(ids=r.ids, weights=r.weights, near_tie=r.near_tie, offsets=offsets,
-                       sorted_slots=sorted_slots, slot_rows=slot_rows, tokens=toks, z=z, o=o, y=y)
+                       sorted_slots=sorted_slots, slot_rows=slot_rows, tokens=toks, z=z, o=o,
+                       y=round_to_bf16_bits(y_f64), y_f64=y_f64)

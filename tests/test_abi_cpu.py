@@ -142,4 +142,5 @@ def test_gemm_checks_the_tiled_layout():
     w0 = moe.Fp4Weights(moe.MOE_FP4_MX, 4, 256, 512, 0x10000, 0x20000, None, moe.MOE_FP4_TILED)
     w1 = moe.Fp4Weights(moe.MOE_FP4_MX, 4, 256, 512, 0x10000, 0x20000, None, 0)
     _err(_gemm(act, w0, w1), moe.MOE_ERR_INVALID)                                # w0 / w1 layouts differ
-    _err(_gemm(act, w0, w0, algo=4), moe.MOE_ERR_INVALID)                        # bad algo
+    _err(_gemm(act, w0, w0, algo=3), moe.MOE_ERR_INVALID)                        # bad algo (no kernel 3)
+    _err(_gemm(act, w0, w0, algo=4), moe.MOE_ERR_INVALID)

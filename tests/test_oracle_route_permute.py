@@ -139,3 +139,41 @@ def test_permute_against_buckets():
         assert off[-1] == T * 8
         for row, slot in enumerate(ss):
             assert sr[slot] == row
+
+
+def _tie_case(gap_expert: float, gap_group: float):
+    """One token whose every routing decision is fixed by construction (all
+    biases are powers of two or small dyadic values, exact in float32):
+    experts with logit 0 have sigmoid exactly 1/2, the others logit -4.
+    Seven experts lead clearly (0, 1, 8, 9, 16, 17, 24); the 8th place goes to
+    expert 2 (1/2 + gap_expert) over expert 3 (1/2); group 3 beats group 4 for
+    the 4th kept group by gap_group (its second expert carries the gap)."""
+    E = 64
+    l = np.full((1, E), -4.0, np.float32)
+    b = np.zeros(E, np.float64)
+    for e, bias in ((0, 0.375), (1, 0.375), (8, 0.25), (9, 0.25), (16, 0.125), (17, 0.125), (24, 0.125),
+                    (32, 0.125), (2, gap_expert), (3, 0.0)):
+        l[0, e] = 0.0
+        b[e] = bias
+    b[25] = gap_group            # logit -4: group 3 = 0.625 + (s + gap), group 4 = 0.625 + s
+    return l, b.astype(np.float32)
+
+
+@pytest.mark.parametrize("gap_expert,gap_group,flag", [
+    (2.0 ** -41, 2.0 ** -4, True),      # 8th/9th expert gap 4.5e-13 < 1e-12
+    (2.0 ** -38, 2.0 ** -4, False),     # 3.6e-12: a clear decision
+    (2.0 ** -4, 2.0 ** -42, True),      # 4th/5th group gap 2.3e-13
+    (2.0 ** -4, 2.0 ** -36, False),     # 1.5e-11
+    (0.0, 2.0 ** -4, False),            # an exact tie is decided by index, not flagged
+])
+def test_near_tie_flag_on_constructed_gaps(gap_expert, gap_group, flag):
+    """near_tie marks exactly the tokens whose 8th/9th expert or 4th/5th group
+    decision has a gap in (0, 1e-12); the decisions themselves go the way the
+    constructed gaps (or, at an exact tie, the lower index) say."""
+    l, b = _tie_case(gap_expert, gap_group)
+    assert np.array_equal(b.astype(np.float64)[[2, 25]], [gap_expert, gap_group])   # exact in float32
+    r = oracle.route(l, b, 8, 4, 8, 2.827)
+    assert bool(r.near_tie[0]) == flag
+    assert sorted(r.ids[0][:7].tolist()) == [0, 1, 8, 9, 16, 17, 24]
+    assert r.ids[0][7] == 2
+    assert sorted({int(e) // 8 for e in r.ids[0]}) == [0, 1, 2, 3]
