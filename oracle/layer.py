@@ -5,10 +5,13 @@ t is W_down,j( SiLU(W_gate,j h_t) (elementwise *) (W_up,j h_t) ), weighted by th
 router's g_{t,j}.  [MOPD-NVFP4] header paragraph: FP32 (here float64)
 accumulation; "Usage" (BF16-activation mode) and "Accuracy": W4A16 (bfloat16
 activations) and W4A4 (NVFP4 activations, unit global scale) variants.
+[PRO6000] "Quantization, context and quality", Activations: the W4A8 variant
+with MXFP8 activations (E4M3, power-of-two scale per 32) for both expert GEMMs.
 
 Roundings happen only where the method stores a narrower type: the layer input
 and output are bfloat16, the expert intermediate z = SiLU(gate) * up is stored
-as bfloat16 and, in W4A4, re-quantised to NVFP4 before the down projection;
+as bfloat16 and, in W4A4 / W4A8, re-quantised to NVFP4 / MXFP8 before the
+down projection;
 everything else is float64.  The combine adds the optional residual and the
 router-weighted expert outputs in slot order j = 0..top_k-1.
 """
@@ -21,7 +24,7 @@ import numpy as np
 
 from .formats import bf16_value, dequant_mx, dequant_nv, round_to_bf16_bits
 from .permute import permute
-from .quant import dequant_nvfp4_act, quantize_nvfp4
+from .quant import dequant_mxfp8, dequant_nvfp4_act, quantize_mxfp8, quantize_nvfp4
 from .route import route
 
 
@@ -35,6 +38,8 @@ def _act_values(bits: np.ndarray, act_mode: str, input_scale: float) -> np.ndarr
     if act_mode == "nvfp4":
         codes, scales = quantize_nvfp4(bits, input_scale)
         return dequant_nvfp4_act(codes, scales, input_scale)
+    if act_mode == "mxfp8":
+        return dequant_mxfp8(*quantize_mxfp8(bits))
     raise ValueError(act_mode)
 
 

@@ -235,3 +235,79 @@ def test_tiny_w4a4_layer_against_brute_force():
             y[t] += wt * (wd @ zq)
     got = oracle.bf16_value(res.y)
     assert np.max(np.abs(got - y)) <= np.max(np.abs(y)) * 2 ** -8
+
+
+# ------------------------------------------------------------------ MXFP8
+def _mxfp8_input(seed=31, rows=67, k=256):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((rows, k)) * 10.0 ** rng.integers(-6, 6, (rows, 1))).astype(np.float32)
+    x[0, :32] = 0.0                              # an all-zero block
+    x[0, 32:64] = -0.0                           # negative zeros
+    x[1, :32] = 1.0
+    x[1, 5] = 2.0 ** 7                           # amax a power of two: maps to exactly 256
+    x[2, :32] = 0.5
+    x[2, 0] = 1.75 * 2 ** 3                      # amax / X = 448 exactly
+    x[3, :32] = 0.25
+    x[3, 0] = 1.875 * 2 ** 3                     # amax / X = 480: saturates at 448
+    x[4, :32] = 2.0 ** -20
+    x[4, 0] = 1.0                                # small elements fall into E4M3 subnormals or to zero
+    return bf16_bits_from_f32(x)
+
+
+def test_mxfp8_codes_match_torch_float8_codec():
+    """Codes are torch's float8_e4m3fn rounding (nearest-even) of x / X after
+    clamping to +-448; scales are E8M0 powers of two; the zero sign follows x."""
+    xb = _mxfp8_input()
+    codes, scales = oracle.quantize_mxfp8(xb)
+    x = oracle.bf16_value(xb)
+    X = np.repeat(np.ldexp(1.0, scales.astype(np.int64) - 127), 32, axis=-1)
+    q = np.clip(x / X, -448.0, 448.0)
+    ref = torch.from_numpy(q.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, ref)
+    # torch's float8 decode agrees with the oracle's dequantisation
+    back = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32).numpy().astype(np.float64) * X
+    assert np.array_equal(oracle.dequant_mxfp8(codes, scales), back)
+
+
+def test_mxfp8_scale_rule_properties():
+    """max|x| / X lies in [256, 512) for every non-zero block (the scale is the
+    power of two that puts the block maximum in E4M3's top binade or saturates
+    it), a zero block gets 2^-127, and the worked cases land where the format says."""
+    xb = _mxfp8_input()
+    codes, scales = oracle.quantize_mxfp8(xb)
+    x = oracle.bf16_value(xb).reshape(xb.shape[0], -1, 32)
+    amax = np.abs(x).max(axis=-1)
+    X = np.ldexp(1.0, scales.astype(np.int64) - 127)
+    nz = amax > 0
+    r = amax[nz] / X[nz]
+    assert np.all((r >= 256) & (r < 512))
+    assert np.all(scales[~nz] == 0)
+    c = codes.reshape(xb.shape[0], -1, 32)
+    assert np.all(c[0, 0] == 0) and np.all(c[0, 1] == 0x80)          # +0 and -0 blocks
+    assert c[1, 0, 5] == 0x78 and scales[1, 0] == 127 + 7 - 8        # 2^7 -> 256 * 2^-1
+    assert c[2, 0, 0] == 0x7E                                        # 448
+    assert c[3, 0, 0] == 0x7E                                        # 480 saturates at 448
+    v = oracle.dequant_mxfp8(codes, scales).reshape(x.shape)
+    assert v[3, 0, 0] == 448 * 2.0 ** -5
+    # 2^-20 with X = 2^-8: 2^-12 < half of E4M3's smallest subnormal 2^-9 -> 0
+    assert np.all(c[4, 0, 1:] == 0)
+
+
+def test_mxfp8_brute_force_nearest():
+    """Every code is the nearest E4M3 value to x / X (ties to the even code),
+    found by search over all 126 finite magnitudes, unless |x / X| > 448."""
+    xb = random_bf16(33, (16, 128), std=3.0)
+    codes, scales = oracle.quantize_mxfp8(xb)
+    x = oracle.bf16_value(xb)
+    X = np.repeat(np.ldexp(1.0, scales.astype(np.int64) - 127), 32, axis=-1)
+    grid = [(Fraction(oracle.e4m3_value(b).item()), b) for b in range(0x7F)]
+    for i in range(x.shape[0]):
+        for j in range(x.shape[1]):
+            t = abs(Fraction(x[i, j]) / Fraction(X[i, j]))
+            if t > 448:
+                want = 0x7E
+            else:
+                best = min(grid, key=lambda gb: (abs(gb[0] - t), gb[1] & 1))
+                want = best[1]
+            want |= 0x80 if np.signbit(x[i, j]) else 0
+            assert codes[i, j] == want, (i, j, x[i, j], codes[i, j], want)
