@@ -25,7 +25,7 @@ MOE_ALGO_AUTO, MOE_ALGO_DECODE, MOE_ALGO_PREFILL = 0, 1, 2
 
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_version", "moe_route", "moe_permute_workspace_bytes",
            "moe_permute", "moe_route_permute", "moe_fp4_grouped_gemm", "moe_combine", "fp4_transcode_mx_to_nv", "moe_quantize_nvfp4",
-           "moe_fp4_tile_weights")
+           "moe_fp4_tile_weights", "moe_route_permute_noalloc")
 
 
 class RouteParams(ctypes.Structure):
@@ -79,6 +79,8 @@ def _load() -> ctypes.CDLL:
     lib.fp4_transcode_mx_to_nv.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp, vp]
     lib.moe_quantize_nvfp4.restype = i32
     lib.moe_quantize_nvfp4.argtypes = [vp, i64, i32, f32, vp, vp, vp, vp]
+    lib.moe_route_permute_noalloc.restype = i32
+    lib.moe_route_permute_noalloc.argtypes = [vp, vp, i64, ctypes.POINTER(RouteParams), vp, vp, vp, vp, vp, vp]
     lib.moe_fp4_tile_weights.restype = i32
     lib.moe_fp4_tile_weights.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
     return lib
@@ -173,6 +175,21 @@ def route_permute(logits: torch.Tensor, bias: Optional[torch.Tensor], num_expert
     _check(lib.moe_route_permute(_ptr(logits), _ptr(bias), T, ctypes.byref(p), _ptr(ids), _ptr(weights),
                                  _ptr(offsets), _ptr(sorted_slots), _ptr(slot_rows), _ptr(counter), _ptr(workspace),
                                  workspace.numel(), _stream(stream)), "moe_route_permute")
+    return ids, weights, offsets, sorted_slots, slot_rows
+
+
+def route_permute_noalloc(logits: torch.Tensor, bias: Optional[torch.Tensor], num_experts: int, n_group: int,
+                          topk_group: int, top_k: int, routed_scaling_factor: float, ids: torch.Tensor,
+                          weights: torch.Tensor, offsets: torch.Tensor, sorted_slots: torch.Tensor,
+                          slot_rows: torch.Tensor, norm_topk_prob: bool = True, stream=None):
+    """route_permute() into caller-provided outputs, with the library's static
+    scratch instead of a counter and workspace (no device allocation)."""
+    _dev(logits, "logits")
+    T = logits.shape[0]
+    p = RouteParams(num_experts, n_group, topk_group, top_k, routed_scaling_factor, int(norm_topk_prob))
+    _check(lib.moe_route_permute_noalloc(_ptr(logits), _ptr(bias), T, ctypes.byref(p), _ptr(ids), _ptr(weights),
+                                         _ptr(offsets), _ptr(sorted_slots), _ptr(slot_rows), _stream(stream)),
+           "moe_route_permute_noalloc")
     return ids, weights, offsets, sorted_slots, slot_rows
 
 

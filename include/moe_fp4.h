@@ -121,6 +121,23 @@ moe_status moe_route_permute(const float* logits, const float* correction_bias, 
                              uint32_t* counter, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+/* ------------------------------------------- route + permute, no allocation
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * outputs, bit for bit, as moe_route_permute, with the hand-off counter and
+ * the permutation's count table in a static device array of the library
+ * (256 B + 256 KiB per GPU, held until the process ends) instead of caller
+ * memory.  The call allocates nothing.  Limit: T * top_k <= 2048 always fits;
+ * larger batches need T * top_k * num_experts <= 2^27 (e.g. 524,288 slots at
+ * 256 experts), else MOE_ERR_UNSUPPORTED and nothing is launched.  All calls
+ * on one GPU share its array: calls that overlap on one GPU (unordered
+ * streams) race.  Other limits and errors as moe_route_permute.
+ */
+moe_status moe_route_permute_noalloc(const float* logits, const float* correction_bias, int64_t T,
+                                     const moe_route_params* p, int32_t* topk_ids, float* topk_weights,
+                                     int32_t* expert_offsets, int32_t* sorted_slots, int32_t* slot_rows,
+                                     hipStream_t stream);
+
 /* ----------------------------------------------------------- grouped GEMM
  * Per expert e and permuted row r in [expert_offsets[e], expert_offsets[e+1]):
  *   MOE_EPI_NONE:   out[r, n]  = sum_k A[r, k] * W0[e, n, k]

@@ -144,3 +144,17 @@ def test_gemm_checks_the_tiled_layout():
     _err(_gemm(act, w0, w1), moe.MOE_ERR_INVALID)                                # w0 / w1 layouts differ
     _err(_gemm(act, w0, w0, algo=3), moe.MOE_ERR_INVALID)                        # bad algo (no kernel 3)
     _err(_gemm(act, w0, w0, algo=4), moe.MOE_ERR_INVALID)
+
+
+def test_route_permute_noalloc_rejects_before_touching_the_gpu():
+    """Bad parameters, NULL pointers and batches beyond the static scratch are
+    refused on the host (no HIP call is made on these paths)."""
+    p = moe.RouteParams(256, 8, 4, 8, 2.827, 1)
+    bad = moe.RouteParams(256, 7, 4, 8, 2.827, 1)
+    f = moe.lib.moe_route_permute_noalloc
+    _err(f(FAKE, None, 4, ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, None), moe.MOE_ERR_INVALID)
+    _err(f(FAKE, None, 4, None, FAKE, FAKE, FAKE, FAKE, FAKE, None), moe.MOE_ERR_INVALID)
+    _err(f(None, None, 4, ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None), moe.MOE_ERR_INVALID)
+    _err(f(FAKE, None, 4, ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, None), moe.MOE_ERR_INVALID)
+    too_many = (1 << 27) // (256 * 8) + 1
+    _err(f(FAKE, None, too_many, ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None), moe.MOE_ERR_UNSUPPORTED)
