@@ -18,14 +18,15 @@ LIB_PATH = os.path.join(_PKG, "libmoefp4.so")
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, 1, 2, 3, 4
 MOE_FP4_MX, MOE_FP4_NV = 0, 1
-MOE_FP4_SCALES_POW2, MOE_FP4_TILED = 1, 2
-MOE_ACT_BF16, MOE_ACT_NVFP4 = 0, 1
+MOE_FP4_SCALES_POW2, MOE_FP4_TILED, MOE_FP4_MX_EXACT = 1, 2, 4
+MOE_ACT_BF16, MOE_ACT_NVFP4, MOE_ACT_MXFP8, MOE_ACT_NVFP4_PLANES = 0, 1, 2, 3
+MOE_OUT_NVFP4, MOE_OUT_MXFP8, MOE_OUT_NVFP4_PLANES = 0, 1, 2
 MOE_EPI_NONE, MOE_EPI_SWIGLU = 0, 1
 MOE_ALGO_AUTO, MOE_ALGO_DECODE, MOE_ALGO_PREFILL = 0, 1, 2
 
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_version", "moe_route", "moe_permute_workspace_bytes",
            "moe_permute", "moe_route_permute", "moe_fp4_grouped_gemm", "moe_combine", "fp4_transcode_mx_to_nv", "moe_quantize_nvfp4",
-           "moe_fp4_tile_weights", "moe_route_permute_noalloc")
+           "moe_fp4_tile_weights", "moe_route_permute_noalloc", "moe_quantize_mxfp8", "moe_quantize_nvfp4_planes")
 
 
 class RouteParams(ctypes.Structure):
@@ -48,7 +49,7 @@ class Act(ctypes.Structure):
 
 class Out(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
-                ("output_scale", ctypes.c_float), ("dequant", ctypes.c_void_p)]
+                ("output_scale", ctypes.c_float), ("dequant", ctypes.c_void_p), ("format", ctypes.c_int32)]
 
 
 def _load() -> ctypes.CDLL:
@@ -81,6 +82,10 @@ def _load() -> ctypes.CDLL:
     lib.moe_quantize_nvfp4.argtypes = [vp, i64, i32, f32, vp, vp, vp, vp]
     lib.moe_route_permute_noalloc.restype = i32
     lib.moe_route_permute_noalloc.argtypes = [vp, vp, i64, ctypes.POINTER(RouteParams), vp, vp, vp, vp, vp, vp]
+    lib.moe_quantize_mxfp8.restype = i32
+    lib.moe_quantize_mxfp8.argtypes = [vp, i64, i32, vp, vp, vp]
+    lib.moe_quantize_nvfp4_planes.restype = i32
+    lib.moe_quantize_nvfp4_planes.argtypes = [vp, i64, i32, f32, vp, vp, vp]
     lib.moe_fp4_tile_weights.restype = i32
     lib.moe_fp4_tile_weights.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
     return lib
@@ -201,6 +206,7 @@ class Weights:
     global_scale: Optional[torch.Tensor] = None   # f32 [E] (NV)
     scales_pow2: bool = False             # NV: every scale byte is 0 or a power of two (a transcode)
     tiled: bool = False                   # codes and scales in the tiled layout (see tile_weights)
+    mx_exact: bool = False                # NV: an exact MXFP4 transcode (E8M0 per 32 exists)
 
     @property
     def format(self):
@@ -210,27 +216,36 @@ class Weights:
         E, n, k2 = self.packed.shape
         return Fp4Weights(self.format, E, n, 2 * k2, self.packed.data_ptr(), self.scale.data_ptr(),
                           None if self.global_scale is None else self.global_scale.data_ptr(),
-                          (MOE_FP4_SCALES_POW2 if self.scales_pow2 else 0) | (MOE_FP4_TILED if self.tiled else 0))
+                          (MOE_FP4_SCALES_POW2 if self.scales_pow2 else 0) | (MOE_FP4_TILED if self.tiled else 0)
+                          | (MOE_FP4_MX_EXACT if self.mx_exact else 0))
+
+
+_ACT_MODES = {"bf16": MOE_ACT_BF16, "nvfp4": MOE_ACT_NVFP4, "mxfp8": MOE_ACT_MXFP8, "planes": MOE_ACT_NVFP4_PLANES}
+_OUT_FORMATS = {"nvfp4": MOE_OUT_NVFP4, "mxfp8": MOE_OUT_MXFP8, "planes": MOE_OUT_NVFP4_PLANES}
 
 
 def grouped_gemm(a: torch.Tensor, w0: Weights, w1: Optional[Weights], offsets: torch.Tensor, rows: int,
                  gather: Optional[torch.Tensor] = None, gather_div: int = 1, a_scales: Optional[torch.Tensor] = None,
                  input_scale: float = 1.0, out: Optional[torch.Tensor] = None, out_codes: Optional[torch.Tensor] = None,
                  out_scales: Optional[torch.Tensor] = None, output_scale: float = 1.0, want_bf16: bool = True,
-                 out_dequant: Optional[torch.Tensor] = None, algo: int = MOE_ALGO_AUTO, stream=None):
-    """A: bf16 [rows_src, k] (W4A16) or NVFP4 codes u8 [rows_src, k/2] with ``a_scales`` (W4A4).
-    ``out_dequant``: bf16 [rows, n] receiving the NVFP4 output's values (codes x scale x output_scale)."""
+                 out_dequant: Optional[torch.Tensor] = None, algo: int = MOE_ALGO_AUTO, a_mode: Optional[str] = None,
+                 out_format: str = "nvfp4", stream=None):
+    """A: bf16 [rows_src, k] (W4A16); NVFP4 codes u8 [rows_src, k/2] with ``a_scales`` (W4A4);
+    ``a_mode="mxfp8"``: E4M3 codes [rows_src, k] + E8M0 [rows_src, k/32] (W4A8);
+    ``a_mode="planes"``: NVFP4 planes [rows_src, 2k] + E8M0 [rows_src, k/16] (W4A4, block-scaled MFMA).
+    ``out_codes``/``out_scales`` receive the output quantised in ``out_format`` ("nvfp4", "mxfp8",
+    "planes"); ``out_dequant``: bf16 [rows, n] receiving an NVFP4 output's values."""
     _dev(a, "a")
     n = w0.packed.shape[1]
     dev = a.device
     if want_bf16 and out is None:
         out = torch.empty((rows, n), dtype=torch.bfloat16, device=dev)
-    act = Act(MOE_ACT_NVFP4 if a_scales is not None else MOE_ACT_BF16, a.data_ptr(),
-              None if a_scales is None else a_scales.data_ptr(), float(input_scale),
+    mode = _ACT_MODES[a_mode] if a_mode is not None else (MOE_ACT_NVFP4 if a_scales is not None else MOE_ACT_BF16)
+    act = Act(mode, a.data_ptr(), None if a_scales is None else a_scales.data_ptr(), float(input_scale),
               None if gather is None else gather.data_ptr(), int(gather_div), a.shape[0])
     o = Out(None if out is None else out.data_ptr(), None if out_codes is None else out_codes.data_ptr(),
             None if out_scales is None else out_scales.data_ptr(), float(output_scale),
-            None if out_dequant is None else out_dequant.data_ptr())
+            None if out_dequant is None else out_dequant.data_ptr(), _OUT_FORMATS[out_format])
     cw0 = w0.c()
     cw1 = w1.c() if w1 is not None else None
     epi = MOE_EPI_SWIGLU if w1 is not None else MOE_EPI_NONE
@@ -273,7 +288,7 @@ def tile_weights(w: Weights, stream=None) -> Weights:
     scale = torch.empty_like(w.scale)
     _check(lib.moe_fp4_tile_weights(w.format, E, n, 2 * k2, _ptr(w.packed), _ptr(w.scale), _ptr(packed), _ptr(scale),
                                     _stream(stream)), "moe_fp4_tile_weights")
-    return Weights(packed, scale, w.global_scale, w.scales_pow2, tiled=True)
+    return Weights(packed, scale, w.global_scale, w.scales_pow2, tiled=True, mx_exact=w.mx_exact)
 
 
 def quantize_nvfp4(x: torch.Tensor, input_scale: float = 1.0, codes=None, scales=None, dequant=None, stream=None):
@@ -285,6 +300,26 @@ def quantize_nvfp4(x: torch.Tensor, input_scale: float = 1.0, codes=None, scales
     _check(lib.moe_quantize_nvfp4(_ptr(x), rows, k, float(input_scale), _ptr(codes), _ptr(scales), _ptr(dequant),
                                   _stream(stream)), "moe_quantize_nvfp4")
     return codes, scales
+
+
+def quantize_mxfp8(x: torch.Tensor, codes=None, scales=None, stream=None):
+    """bf16 [rows, k] -> (E4M3 codes u8 [rows, k], E8M0 scales u8 [rows, k/32])."""
+    rows, k = x.shape
+    codes = torch.empty((rows, k), dtype=torch.uint8, device=x.device) if codes is None else codes
+    scales = torch.empty((rows, k // 32), dtype=torch.uint8, device=x.device) if scales is None else scales
+    _check(lib.moe_quantize_mxfp8(_ptr(x), rows, k, _ptr(codes), _ptr(scales), _stream(stream)), "moe_quantize_mxfp8")
+    return codes, scales
+
+
+def quantize_nvfp4_planes(x: torch.Tensor, input_scale: float = 1.0, planes=None, scales=None, stream=None):
+    """bf16 [rows, k] -> (E4M3 planes u8 [rows, 2k], E8M0 scales u8 [rows, k/16]): the NVFP4
+    quantisation of x in the block-scaled MFMA's operand form."""
+    rows, k = x.shape
+    planes = torch.empty((rows, 2 * k), dtype=torch.uint8, device=x.device) if planes is None else planes
+    scales = torch.empty((rows, k // 16), dtype=torch.uint8, device=x.device) if scales is None else scales
+    _check(lib.moe_quantize_nvfp4_planes(_ptr(x), rows, k, float(input_scale), _ptr(planes), _ptr(scales),
+                                         _stream(stream)), "moe_quantize_nvfp4_planes")
+    return planes, scales
 
 
 from .layer import MoELayer, LayerWeights  # noqa: E402  (composition of the calls above)

@@ -37,6 +37,9 @@ moe_status launch_quant(const void*, int64_t, int, float, uint8_t*, uint8_t*, vo
 moe_status launch_tile(bool, int64_t, int, int, const uint8_t*, const uint8_t*, uint8_t*, uint8_t*, hipStream_t);
 moe_status launch_gemm_decode(const GemmArgs&, bool swiglu, int wf, bool a_nv, int64_t rows, hipStream_t);
 moe_status launch_gemm_prefill(const GemmArgs&, bool swiglu, int wf, bool a_nv, int64_t rows, hipStream_t);
+moe_status launch_gemm_scaled(const GemmArgs&, bool swiglu, bool planes, bool w_nv, hipStream_t);
+moe_status launch_quant_mxfp8(const void*, int64_t, int, uint8_t*, uint8_t*, hipStream_t);
+moe_status launch_quant_planes(const void*, int64_t, int, float, uint8_t*, uint8_t*, hipStream_t);
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -161,8 +164,10 @@ static moe_status check_weights(const moe_fp4_weights* w, const char* name) {
   MOE_CHECK(w->packed && w->scale, "moe_fp4_grouped_gemm: %s NULL data", name);
   MOE_CHECK(aligned16(w->packed), "moe_fp4_grouped_gemm: %s codes not 16-byte aligned", name);
   if (w->format == MOE_FP4_NV) MOE_CHECK(w->global_scale != nullptr, "moe_fp4_grouped_gemm: %s NV without global", name);
-  MOE_CHECK((w->flags & ~(MOE_FP4_SCALES_POW2 | MOE_FP4_TILED)) == 0, "moe_fp4_grouped_gemm: %s unknown flags 0x%x",
-            name, w->flags);
+  MOE_CHECK((w->flags & ~(MOE_FP4_SCALES_POW2 | MOE_FP4_TILED | MOE_FP4_MX_EXACT)) == 0,
+            "moe_fp4_grouped_gemm: %s unknown flags 0x%x", name, w->flags);
+  MOE_CHECK(w->format == MOE_FP4_NV || (w->flags & (MOE_FP4_SCALES_POW2 | MOE_FP4_MX_EXACT)) == 0,
+            "moe_fp4_grouped_gemm: %s scale flags are for NV weights", name);
   if (w->k % 128 != 0 || w->n % 16 != 0) {
     set_error("moe_fp4_grouped_gemm: %s needs k %% 128 == 0 and n %% 16 == 0 (n=%d k=%d)", name, w->n, w->k);
     return MOE_ERR_UNSUPPORTED;
@@ -190,25 +195,55 @@ moe_status moe_fp4_grouped_gemm(const moe_act* a, const moe_fp4_weights* w0, con
               "moe_fp4_grouped_gemm: w0 / w1 differ");
   }
   MOE_CHECK(rows >= 0, "moe_fp4_grouped_gemm: rows < 0");
-  MOE_CHECK(a->mode == MOE_ACT_BF16 || a->mode == MOE_ACT_NVFP4, "moe_fp4_grouped_gemm: bad activation mode");
+  MOE_CHECK(a->mode >= MOE_ACT_BF16 && a->mode <= MOE_ACT_NVFP4_PLANES, "moe_fp4_grouped_gemm: bad activation mode");
   MOE_CHECK(a->data != nullptr && aligned16(a->data), "moe_fp4_grouped_gemm: activation data NULL or unaligned");
-  if (a->mode == MOE_ACT_NVFP4) {
-    MOE_CHECK(a->scales != nullptr, "moe_fp4_grouped_gemm: NVFP4 activations need scales");
+  const bool scaled = a->mode == MOE_ACT_MXFP8 || a->mode == MOE_ACT_NVFP4_PLANES;
+  if (a->mode != MOE_ACT_BF16) MOE_CHECK(a->scales != nullptr, "moe_fp4_grouped_gemm: activations need scales");
+  if (a->mode == MOE_ACT_NVFP4)
     MOE_CHECK(is_pow2_float(a->input_scale), "moe_fp4_grouped_gemm: input_scale must be a power of two");
-  }
   if (a->gather) MOE_CHECK(a->gather_div >= 1, "moe_fp4_grouped_gemm: gather_div < 1");
   MOE_CHECK(a->rows_src >= 0, "moe_fp4_grouped_gemm: rows_src < 0");
-  if (a->rows_src * (int64_t)w0->k * 2 >= ((int64_t)1 << 31)) {
+  // bytes per source row of the token operand
+  const int64_t a_row_bytes = a->mode == MOE_ACT_BF16 ? (int64_t)w0->k * 2
+                              : a->mode == MOE_ACT_NVFP4 ? (int64_t)w0->k / 2
+                              : a->mode == MOE_ACT_MXFP8 ? (int64_t)w0->k : (int64_t)w0->k * 2;
+  if (a->rows_src * a_row_bytes >= ((int64_t)1 << 31)) {
     set_error("moe_fp4_grouped_gemm: activations larger than 2 GiB are not supported");
     return MOE_ERR_UNSUPPORTED;
   }
   MOE_CHECK(out->data || out->codes || out->dequant, "moe_fp4_grouped_gemm: no output");
+  MOE_CHECK(out->format >= MOE_OUT_NVFP4 && out->format <= MOE_OUT_NVFP4_PLANES, "moe_fp4_grouped_gemm: bad out.format");
   if (out->data) MOE_CHECK(aligned16(out->data), "moe_fp4_grouped_gemm: output not 16-byte aligned");
-  if (out->dequant) MOE_CHECK(aligned16(out->dequant), "moe_fp4_grouped_gemm: dequant output not 16-byte aligned");
-  if (out->codes) MOE_CHECK(out->scales != nullptr, "moe_fp4_grouped_gemm: NVFP4 output needs scales");
+  if (out->dequant) {
+    MOE_CHECK(aligned16(out->dequant), "moe_fp4_grouped_gemm: dequant output not 16-byte aligned");
+    MOE_CHECK(out->format == MOE_OUT_NVFP4, "moe_fp4_grouped_gemm: dequant output is for the NVFP4 format");
+  }
+  if (out->codes) MOE_CHECK(out->scales != nullptr, "moe_fp4_grouped_gemm: quantised output needs scales");
   if (out->codes || out->dequant)
     MOE_CHECK(is_pow2_float(out->output_scale), "moe_fp4_grouped_gemm: output_scale must be a power of two");
+  if (out->format != MOE_OUT_NVFP4) {
+    MOE_CHECK(out->codes != nullptr, "moe_fp4_grouped_gemm: MXFP8 / plane output needs codes");
+    MOE_CHECK(((uintptr_t)out->codes & 3) == 0, "moe_fp4_grouped_gemm: MXFP8 / plane codes not 4-byte aligned");
+    if (out->format == MOE_OUT_MXFP8) MOE_CHECK(w0->n % 32 == 0, "moe_fp4_grouped_gemm: MXFP8 output needs n %% 32 == 0");
+    int e;
+    (void)frexpf(out->output_scale, &e);
+    MOE_CHECK(e - 1 >= -100 && e - 1 <= 100, "moe_fp4_grouped_gemm: output_scale outside [2^-100, 2^100]");
+    if (!scaled) {
+      set_error("moe_fp4_grouped_gemm: MXFP8 / plane outputs come from the MXFP8 / plane activation modes");
+      return MOE_ERR_UNSUPPORTED;
+    }
+  }
   MOE_CHECK(algo >= MOE_ALGO_AUTO && algo <= MOE_ALGO_PREFILL, "moe_fp4_grouped_gemm: bad algo");
+  if (scaled) {
+    MOE_CHECK(w0->format == MOE_FP4_MX || (w0->flags & MOE_FP4_MX_EXACT),
+              "moe_fp4_grouped_gemm: block-scaled MFMA modes need MX weights or NV weights flagged MX_EXACT");
+      const int bn = epi == MOE_EPI_SWIGLU ? 256 : 512;
+    if (w0->n % bn != 0 || w0->k % 256 != 0 || w0->num_experts > 1000) {
+      set_error("moe_fp4_grouped_gemm: block-scaled MFMA modes need n %% %d == 0, k %% 256 == 0 and <= 1000 experts "
+                "(n=%d k=%d E=%d)", bn, w0->n, w0->k, w0->num_experts);
+      return MOE_ERR_UNSUPPORTED;
+    }
+  }
   if (rows == 0) return MOE_OK;
 
   GemmArgs g;
@@ -217,7 +252,7 @@ moe_status moe_fp4_grouped_gemm(const moe_act* a, const moe_fp4_weights* w0, con
   g.a_scales = a->scales;
   g.a_gscale = a->mode == MOE_ACT_NVFP4 ? a->input_scale : 1.0f;
   g.gather = a->gather;
-  g.a_bytes = a->rows_src * (a->mode == MOE_ACT_NVFP4 ? (int64_t)(w0->k / 2) : (int64_t)w0->k * 2);
+  g.a_bytes = a->rows_src * a_row_bytes;
   g.gather_div = a->gather ? a->gather_div : 1;
   g.w_packed[0] = w0->packed;
   g.w_scale[0] = w0->scale;
@@ -238,11 +273,18 @@ moe_status moe_fp4_grouped_gemm(const moe_act* a, const moe_fp4_weights* w0, con
   g.out_inv_g = nvfp4_out ? 1.0f / out->output_scale : 1.0f;
   g.out_dq = (uint16_t*)out->dequant;
   g.out_g = nvfp4_out ? out->output_scale : 1.0f;
+  g.out_format = out->format;
+  {
+    int e;
+    (void)frexpf(g.out_g, &e);
+    g.out_g_log2 = e - 1;
+  }
   g.tiled = (w0->flags & MOE_FP4_TILED) != 0;
 
   const bool swiglu = epi == MOE_EPI_SWIGLU;
+  if (scaled) return launch_gemm_scaled(g, swiglu, a->mode == MOE_ACT_NVFP4_PLANES, w0->format == MOE_FP4_NV, stream);
   // weight scale format: 0 MXFP4, 1 NVFP4 with power-of-two scales, 2 NVFP4 with any scales
-  const int wf = w0->format == MOE_FP4_MX ? 0 : ((w0->flags & MOE_FP4_SCALES_POW2) ? 1 : 2);
+  const int wf = w0->format == MOE_FP4_MX ? 0 : ((w0->flags & (MOE_FP4_SCALES_POW2 | MOE_FP4_MX_EXACT)) ? 1 : 2);
   const bool a_nv = a->mode == MOE_ACT_NVFP4;
   int use = algo;
   if (use == MOE_ALGO_AUTO) use = (rows >= 32LL * g.E) ? MOE_ALGO_PREFILL : MOE_ALGO_DECODE;
@@ -311,6 +353,30 @@ moe_status moe_quantize_nvfp4(const void* x, int64_t rows, int32_t k, float inpu
   MOE_CHECK(aligned16(x) && ((uintptr_t)codes & 7u) == 0, "moe_quantize_nvfp4: misaligned buffers");
   if (dequant) MOE_CHECK(aligned16(dequant), "moe_quantize_nvfp4: dequant output not 16-byte aligned");
   return launch_quant(x, rows, k, input_scale, codes, scales, dequant, stream);
+}
+
+moe_status moe_quantize_mxfp8(const void* x, int64_t rows, int32_t k, uint8_t* codes, uint8_t* scales,
+                              hipStream_t stream) {
+  g_err[0] = 0;
+  MOE_CHECK(rows >= 0 && k >= 32 && k % 32 == 0, "moe_quantize_mxfp8: needs k %% 32 == 0");
+  if (rows == 0) return MOE_OK;
+  MOE_CHECK(x && codes && scales, "moe_quantize_mxfp8: NULL pointer");
+  MOE_CHECK(aligned16(x) && aligned16(codes), "moe_quantize_mxfp8: misaligned buffers");
+  return launch_quant_mxfp8(x, rows, k, codes, scales, stream);
+}
+
+moe_status moe_quantize_nvfp4_planes(const void* x, int64_t rows, int32_t k, float input_scale, uint8_t* planes,
+                                     uint8_t* plane_scales, hipStream_t stream) {
+  g_err[0] = 0;
+  MOE_CHECK(rows >= 0 && k >= 32 && k % 32 == 0, "moe_quantize_nvfp4_planes: needs k %% 32 == 0");
+  MOE_CHECK(is_pow2_float(input_scale), "moe_quantize_nvfp4_planes: input_scale must be a power of two");
+  int e;
+  (void)frexpf(input_scale, &e);
+  MOE_CHECK(e - 1 >= -100 && e - 1 <= 100, "moe_quantize_nvfp4_planes: input_scale outside [2^-100, 2^100]");
+  if (rows == 0) return MOE_OK;
+  MOE_CHECK(x && planes && plane_scales, "moe_quantize_nvfp4_planes: NULL pointer");
+  MOE_CHECK(aligned16(x) && aligned16(planes), "moe_quantize_nvfp4_planes: misaligned buffers");
+  return launch_quant_planes(x, rows, k, input_scale, planes, plane_scales, stream);
 }
 
 }  // extern "C"

@@ -11,6 +11,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
 namespace moe {
 
@@ -198,6 +199,63 @@ __device__ __forceinline__ uint32_t quant16(const float* x, float inv_g, uint32_
   lo = w[0];
   hi = w[1];
   return sb;
+}
+
+// ------------------------------------------------------------- MXFP8
+// floor(log2 a) for a finite float a > 0, normal or subnormal
+__device__ __forceinline__ int floor_log2_f32(float a) {
+  const uint32_t u = __float_as_uint(a);
+  const int e = (int)((u >> 23) & 0xFFu);
+  if (e) return e - 127;
+  return (31 - (int)__clz(u & 0x7FFFFFu)) - 149;
+}
+
+// Shared-scale exponent of an MXFP8 block (OCP Microscaling rule): floor(log2
+// amax) minus 8 (the exponent of E4M3's largest power of two), kept in E8M0's
+// range; an all-zero block gets 2^-127.
+__device__ __forceinline__ int mxfp8_scale_exp(float amax) {
+  if (!(amax > 0.0f)) return -127;
+  const int e = floor_log2_f32(amax) - 8;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// 2^e as a float, exactly, for e in [-127, 127]
+__device__ __forceinline__ float exp2_int(int e) {
+  return e >= -126 ? __uint_as_float((uint32_t)(e + 127) << 23) : __uint_as_float(0x00400000u);
+}
+
+// Signed E4M3 code of v: magnitude rounded to nearest-even, saturating at 448;
+// the sign bit follows v (so -0 and small negatives give 0x80).
+__device__ __forceinline__ uint32_t e4m3_code_signed(float v) {
+  return f32_to_e4m3_sat(fabsf(v)) | ((__float_as_uint(v) >> 24) & 0x80u);
+}
+
+// --------------------------------------------- NVFP4 as two E4M3 planes
+// An NVFP4 value c * s (E2M1 code c, E4M3 scale s = 2^k (lead + f1/2 +
+// (2 f2 + f3)/8), k = max(exponent field, 1) - 7) is hi + lo times 2^(k-1) with
+// hi = c (2 lead + f1) and lo = c (2 f2 + f3) / 4, both exact E4M3 values
+// (every scale byte and code checked with exact rationals).  Four codes
+// (16 bits, element 0 in the low nibble) -> four hi bytes and four lo bytes;
+// the values are exact, so the hardware FP8 convert's rounding never acts.
+__device__ __forceinline__ void nvfp4_planes4(uint32_t bits, uint32_t sb, uint32_t& hi, uint32_t& lo) {
+  const uint32_t e = (sb >> 3) & 15u, m = sb & 7u;
+  const float mh = (float)(2u * (e > 0u ? 1u : 0u) + ((m >> 2) & 1u));
+  const float ml = (float)(2u * ((m >> 1) & 1u) + (m & 1u)) * 0.25f;
+  const f32x2 c01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(bits, 1.0f, 0);
+  const f32x2 c23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(bits, 1.0f, 1);
+  int h = __builtin_amdgcn_cvt_pk_fp8_f32(c01[0] * mh, c01[1] * mh, 0, false);
+  h = __builtin_amdgcn_cvt_pk_fp8_f32(c23[0] * mh, c23[1] * mh, h, true);
+  int l = __builtin_amdgcn_cvt_pk_fp8_f32(c01[0] * ml, c01[1] * ml, 0, false);
+  l = __builtin_amdgcn_cvt_pk_fp8_f32(c23[0] * ml, c23[1] * ml, l, true);
+  hi = (uint32_t)h;
+  lo = (uint32_t)l;
+}
+
+// E8M0 byte of the planes' shared scale 2^(k-1) * g, g = 2^g_log2
+__device__ __forceinline__ uint32_t nvfp4_plane_scale(uint32_t sb, int g_log2) {
+  const int e = (int)((sb >> 3) & 15u);
+  const int k = (e > 1 ? e : 1) - 7;
+  return (uint32_t)(k - 1 + g_log2 + 127);
 }
 
 }  // namespace moe

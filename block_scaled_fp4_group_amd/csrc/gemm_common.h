@@ -26,6 +26,8 @@ struct GemmArgs {
   float out_inv_g;                // 1 / output global scale
   uint16_t* out_dq;               // [rows, N] bf16 NVFP4 values (codes x scale x global) or null
   float out_g;                    // output global scale
+  int out_format;                 // MOE_OUT_NVFP4 / MOE_OUT_MXFP8 / MOE_OUT_NVFP4_PLANES (codes, scales)
+  int out_g_log2;                 // log2(out_g) (NVFP4 planes: folded into their E8M0 scales)
   int tiled;                      // weights in the tiled layout (host-side dispatch)
 };
 

@@ -10,7 +10,12 @@ both GEMMs then multiply the NVFP4 values themselves, handed over as exact
 bfloat16 (code x scale x global has at most 6 significant bits), so they run
 the bf16-input kernels on exactly the W4A4 operands.  ``a_mode="nvfp4_codes"``
 feeds the GEMMs the NVFP4 codes and scales instead (the same products, with
-the dequantisation inside the GEMM).
+the dequantisation inside the GEMM); ``a_mode="planes"`` feeds them the same
+NVFP4 values as two exact E4M3 planes under E8M0 scales, on the block-scaled
+MFMA with the FP4 weights as its native operand.
+
+W4A8 (``act_mode="mxfp8"``): x is quantised to MXFP8 and the gate/up epilogue
+quantises the bf16 z to MXFP8; both GEMMs run on the block-scaled MFMA.
 """
 from __future__ import annotations
 
@@ -19,8 +24,8 @@ from typing import Optional
 
 import torch
 
-from . import (MOE_ALGO_AUTO, Weights, combine, grouped_gemm, permute_workspace_bytes, quantize_nvfp4,
-               route_permute)
+from . import (MOE_ALGO_AUTO, Weights, combine, grouped_gemm, permute_workspace_bytes, quantize_mxfp8,
+               quantize_nvfp4, quantize_nvfp4_planes, route_permute)
 
 
 @dataclasses.dataclass
@@ -55,6 +60,16 @@ class MoELayer:
         self.counter = torch.zeros(1, dtype=i32, device=dev)   # router -> permutation hand-off (left zero)
         self.o = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
         self.y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        if act_mode == "mxfp8" or (act_mode == "nvfp4" and a_mode == "planes"):
+            planes = act_mode == "nvfp4"
+            kx, kz = (2 * H, 2 * I) if planes else (H, I)
+            sx, sz = (H // 16, I // 16) if planes else (H // 32, I // 32)
+            self.x_q = torch.empty((T, kx), dtype=torch.uint8, device=dev)
+            self.x_qs = torch.empty((T, sx), dtype=torch.uint8, device=dev)
+            self.z_q = torch.empty((R, kz), dtype=torch.uint8, device=dev)
+            self.z_qs = torch.empty((R, sz), dtype=torch.uint8, device=dev)
+            self.z = torch.empty((R, I), dtype=torch.bfloat16, device=dev) if keep_z_bf16 else None
+            return
         w4a4 = act_mode == "nvfp4"
         self.z = torch.empty((R, I), dtype=torch.bfloat16, device=dev) if (not w4a4 or keep_z_bf16) else None
         if w4a4:
@@ -83,7 +98,24 @@ class MoELayer:
                       sorted_slots=self.sorted_slots[:R], slot_rows=self.slot_rows[:R])
         z = None if self.z is None else self.z[:R]
         o = self.o[:R]
-        if self.act_mode == "nvfp4" and self.a_mode == "dequant":
+        if self.act_mode == "mxfp8" or (self.act_mode == "nvfp4" and self.a_mode == "planes"):
+            planes = self.act_mode == "nvfp4"
+            if planes:
+                quantize_nvfp4_planes(x, self.input_scale, self.x_q[:T], self.x_qs[:T])
+            else:
+                quantize_mxfp8(x, self.x_q[:T], self.x_qs[:T])
+            am = "planes" if planes else "mxfp8"
+            mark("gate_up", 0)
+            grouped_gemm(self.x_q[:T], self.w.gate, self.w.up, self.offsets, R, gather=self.sorted_slots[:R],
+                         gather_div=self.top_k, a_scales=self.x_qs[:T], out=z, out_codes=self.z_q[:R],
+                         out_scales=self.z_qs[:R], output_scale=self.input_scale if planes else 1.0,
+                         want_bf16=z is not None, algo=algo, a_mode=am, out_format=am)
+            mark("gate_up", 1)
+            mark("down", 0)
+            grouped_gemm(self.z_q[:R], self.w.down, None, self.offsets, R, a_scales=self.z_qs[:R], out=o, algo=algo,
+                         a_mode=am)
+            mark("down", 1)
+        elif self.act_mode == "nvfp4" and self.a_mode == "dequant":
             xdq = self.x_dq[:T]
             quantize_nvfp4(x, self.input_scale, self.x_codes[:T], self.x_scales[:T], dequant=xdq)
             keep = z is not None

@@ -143,9 +143,18 @@ moe_status moe_route_permute_noalloc(const float* logits, const float* correctio
  *   MOE_EPI_NONE:   out[r, n]  = sum_k A[r, k] * W0[e, n, k]
  *   MOE_EPI_SWIGLU: out[r, n]  = SiLU(sum_k A[r,k] W0[e,n,k]) * (sum_k A[r,k] W1[e,n,k])
  * with exact dequantised operands and FP32 accumulation.  The result is
- * rounded to bfloat16 (out.data) and/or quantised to NVFP4 from that
- * bfloat16 value (out.codes/out.scales, with global out.output_scale).
+ * rounded to bfloat16 (out.data) and/or quantised from that bfloat16 value
+ * (out.codes/out.scales in out.format: NVFP4, MXFP8 or NVFP4 planes).
  * Rows r >= expert_offsets[E] (and < rows) are not written.
+ *
+ * Kernels: bf16 and NVFP4-code activations run on bf16 MFMA after exact
+ * in-register dequantisation (FP4 x scale has <= 6 significant bits); MXFP8
+ * and NVFP4-plane activations run on gfx950's block-scaled MFMA
+ * (V_MFMA_SCALE_F32_16X16X128_F8F6F4) with the FP4 weights as the native
+ * E2M1 operand under their E8M0 scales.  W4A8 with MXFP8 activations is the
+ * prompt path of "MiMo-V2.6-Flash-MOPD on one RTX PRO 6000" ("Quantization,
+ * context and quality", Activations: E4M3 with a power-of-two scale per 32
+ * values; "What makes it fast", speed v5.2: FP8 x FP4 block-scaled GEMMs).
  */
 typedef enum { MOE_FP4_MX = 0, MOE_FP4_NV = 1 } moe_fp4_format;
 
@@ -160,6 +169,14 @@ typedef enum { MOE_FP4_MX = 0, MOE_FP4_NV = 1 } moe_fp4_format;
                                  k % 512 == 0); same values, bit-identical results, and
                                  every weight load of the kernels reads one contiguous
                                  block */
+#define MOE_FP4_MX_EXACT 4    /* NV: the weights are an exact MXFP4 transcode (what
+                                 fp4_transcode_mx_to_nv writes): both E4M3 scales of each
+                                 32-block are the same power of two (zero only over
+                                 all-zero codes) and the global scale is a power of two,
+                                 so every 32-block has an E8M0 scale.  Required for NV
+                                 weights with MXFP8 / NVFP4-plane activations (the
+                                 block-scaled MFMA takes E8M0 per 32); implies
+                                 MOE_FP4_SCALES_POW2. */
 
 typedef struct {
   moe_fp4_format format;
@@ -169,7 +186,7 @@ typedef struct {
   const uint8_t* packed;      /* codes [E, n, k/2] ("weight_packed")                    */
   const uint8_t* scale;       /* MX: E8M0 [E, n, k/32] | NV: E4M3 [E, n, k/16]          */
   const float* global_scale;  /* NV: float [E] (per expert matrix) | MX: NULL            */
-  int32_t flags;              /* MOE_FP4_SCALES_POW2 (NV only) | MOE_FP4_TILED, or 0     */
+  int32_t flags;              /* MOE_FP4_SCALES_POW2 | MOE_FP4_MX_EXACT (NV only) | MOE_FP4_TILED */
 } moe_fp4_weights;
 
 /* Rearrange expert weights into the tiled layout (flag MOE_FP4_TILED): the
@@ -191,13 +208,25 @@ moe_status moe_fp4_tile_weights(moe_fp4_format format, int32_t num_experts, int3
                                 const uint8_t* packed, const uint8_t* scale, uint8_t* packed_tiled,
                                 uint8_t* scale_tiled, hipStream_t stream);
 
-typedef enum { MOE_ACT_BF16 = 0 /* W4A16 */, MOE_ACT_NVFP4 = 1 /* W4A4 */ } moe_act_mode;
+/* Activation modes.  MXFP8 and NVFP4 planes run on the block-scaled MFMA and
+ * need: MX weights or NV weights flagged MOE_FP4_MX_EXACT; n a multiple of 512
+ * (one matrix) or 256 (SwiGLU, per matrix); k % 256 == 0; num_experts <= 1000.
+ * Other shapes return MOE_ERR_UNSUPPORTED.
+ *   MOE_ACT_MXFP8:        data = E4M3 codes u8 [rows_src, k], scales = E8M0
+ *                         u8 [rows_src, k/32] (moe_quantize_mxfp8)
+ *   MOE_ACT_NVFP4_PLANES: data = E4M3 planes u8 [rows_src, 2k], scales = E8M0
+ *                         u8 [rows_src, k/16]: NVFP4 values, the global scale
+ *                         folded in (moe_quantize_nvfp4_planes)               */
+typedef enum {
+  MOE_ACT_BF16 = 0 /* W4A16 */, MOE_ACT_NVFP4 = 1 /* W4A4, codes */, MOE_ACT_MXFP8 = 2 /* W4A8 */,
+  MOE_ACT_NVFP4_PLANES = 3 /* W4A4 on the block-scaled MFMA */
+} moe_act_mode;
 
 typedef struct {
   moe_act_mode mode;
-  const void* data;           /* BF16: bf16 [rows_src, k] | NVFP4: codes u8 [rows_src, k/2] */
-  const uint8_t* scales;      /* NVFP4: E4M3 [rows_src, k/16] | BF16: NULL               */
-  float input_scale;          /* NVFP4 global scale (a power of two; 1.0 = unit scale)   */
+  const void* data;           /* BF16: bf16 [rows_src, k] | NVFP4: codes u8 [rows_src, k/2] | see above */
+  const uint8_t* scales;      /* NVFP4: E4M3 [rows_src, k/16] | BF16: NULL | see above   */
+  float input_scale;          /* NVFP4 global scale (a power of two; 1.0 = unit scale); 1.0 otherwise */
   const int32_t* gather;      /* NULL: row r reads source row r; else gather[r] / gather_div */
   int32_t gather_div;
   int64_t rows_src;
@@ -205,15 +234,23 @@ typedef struct {
 
 typedef enum { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU = 1 } moe_epilogue;
 
+/* moe_out.format: what out.codes / out.scales hold */
+#define MOE_OUT_NVFP4 0        /* codes [rows, n/2] E2M1, scales [rows, n/16] E4M3, global output_scale */
+#define MOE_OUT_MXFP8 1        /* codes [rows, n] E4M3, scales [rows, n/32] E8M0 (needs n % 32 == 0) */
+#define MOE_OUT_NVFP4_PLANES 2 /* codes [rows, 2n] E4M3 planes, scales [rows, n/16] E8M0: the NVFP4
+                                  quantisation with global output_scale, as moe_quantize_nvfp4_planes */
+
 typedef struct {
   void* data;                 /* bf16 [rows, n] or NULL                                   */
-  uint8_t* codes;             /* NVFP4 codes [rows, n/2] or NULL (needs n % 16 == 0)       */
-  uint8_t* scales;            /* E4M3 [rows, n/16] (with codes)                           */
-  float output_scale;         /* global scale of the NVFP4 output (a power of two)        */
-  void* dequant;              /* bf16 [rows, n] or NULL: the NVFP4 values themselves,
-                                 codes x scale x output_scale (exact in bfloat16), so a
-                                 following bf16-input GEMM computes on exactly the NVFP4
-                                 operand (W4A4 down projection)                         */
+  uint8_t* codes;             /* quantised output (see format) or NULL (needs n % 16 == 0) */
+  uint8_t* scales;            /* its scales (with codes)                                  */
+  float output_scale;         /* global scale of an NVFP4 output (a power of two)         */
+  void* dequant;              /* bf16 [rows, n] or NULL (NVFP4 format only): the NVFP4
+                                 values themselves, codes x scale x output_scale (exact in
+                                 bfloat16), so a following bf16-input GEMM computes on
+                                 exactly the NVFP4 operand (W4A4 down projection)       */
+  int32_t format;             /* MOE_OUT_*: MXFP8 and planes only from the MXFP8 /
+                                 NVFP4-plane activation modes                             */
 } moe_out;
 
 #define MOE_ALGO_AUTO 0       /* choose by rows per expert                                */
@@ -271,6 +308,33 @@ moe_status fp4_transcode_mx_to_nv(const uint8_t* mx_scale, const uint8_t* packed
  */
 moe_status moe_quantize_nvfp4(const void* x, int64_t rows, int32_t k, float input_scale,
                               uint8_t* codes, uint8_t* scales, void* dequant, hipStream_t stream);
+
+/* ---------------------------------------------------- MXFP8 quantisation
+ * W4A8 activations ("MiMo-V2.6-Flash-MOPD on one RTX PRO 6000", "Quantization,
+ * context and quality", Activations: E4M3 with a power-of-two scale per 32
+ * values).  Per row and 32-element block of bf16 x: X = 2^(floor(log2
+ * max|x|) - 8) (the OCP Microscaling rule; 2^-127 for a zero block), codes =
+ * E4M3_rne(x / X) saturated at +-448 with the sign of x; scales = E8M0 of X.
+ *   x bf16 [rows, k]; codes u8 [rows, k]; scales u8 [rows, k/32]; k % 32 == 0;
+ *   x and codes 16-byte aligned.  rows == 0 is a no-op.
+ */
+moe_status moe_quantize_mxfp8(const void* x, int64_t rows, int32_t k, uint8_t* codes, uint8_t* scales,
+                              hipStream_t stream);
+
+/* ----------------------------------------- NVFP4 as block-scaled planes
+ * The NVFP4 quantisation of moe_quantize_nvfp4, in the form the block-scaled
+ * MFMA takes (an NVFP4 scale is an arbitrary E4M3 per 16 values; the MFMA
+ * takes E8M0 per 32).  Each 16-value block with E2M1 codes c_i and E4M3 scale
+ * s = 2^e (lead + f1/2 + (2 f2 + f3)/8) (e = max(exponent field, 1) - 7)
+ * becomes 32 E4M3 bytes, hi_i = c_i (2 lead + f1) then lo_i = c_i (2 f2 + f3) / 4,
+ * and one E8M0 scale 2^(e-1) * input_scale: (hi_i + lo_i) * scale equals the
+ * NVFP4 value c_i * s * input_scale exactly.
+ *   x bf16 [rows, k]; planes u8 [rows, 2k]; plane_scales u8 [rows, k/16];
+ *   k % 32 == 0; input_scale a power of two in [2^-100, 2^100]; x and planes
+ *   16-byte aligned.  rows == 0 is a no-op.
+ */
+moe_status moe_quantize_nvfp4_planes(const void* x, int64_t rows, int32_t k, float input_scale, uint8_t* planes,
+                                     uint8_t* plane_scales, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -11,6 +11,10 @@ straddle a boundary between the persistent kernels' per-XCD slices of work.
 
 The layer output y is held to the stated bound literally: max|y - y64| <=
 2e-2 * rms(y64) against the oracle's float64 sum y64 before its bf16 rounding.
+For W4A8 (MXFP8 z, not one of the five workloads) the bound is asserted
+step-wise and the end-to-end figures are reported: a one-ulp difference in
+the bf16 z between FP32 and float64 accumulation can move an E4M3 code of z by
+a whole step.
 The stored intermediates z and o are compared element by element within
 max(2e-2 * rms, one bf16 ulp of the reference): each is one bf16 rounding of a
 sum that the GPU forms in FP32 and the oracle in float64, so the two may sit on
@@ -55,16 +59,40 @@ def upload_weights(W, fmt):
     return moe.LayerWeights(one("gate"), one("up"), one("down"))
 
 
+def gpu_down_input(layer, rows, zb, act_mode, a_mode):
+    """The down projection's input values for permuted rows `rows`, read from the
+    GPU's quantised z after checking that it is exactly the oracle's
+    quantisation of the GPU's own bf16 z (zb)."""
+    if act_mode == "mxfp8":
+        zc, zs = host(layer.z_q[rows]), host(layer.z_qs[rows])
+        c_ref, s_ref = oracle.quantize_mxfp8(zb)
+        assert np.array_equal(zc, c_ref) and np.array_equal(zs, s_ref)
+        return oracle.dequant_mxfp8(zc, zs)
+    if act_mode == "nvfp4":
+        c_ref, s_ref = oracle.quantize_nvfp4(zb, 1.0)
+        want = oracle.dequant_nvfp4_act(c_ref, s_ref)
+        if a_mode == "planes":
+            from test_gpu_scaled import decode_planes
+            got = decode_planes(host(layer.z_q[rows]), host(layer.z_qs[rows]))
+        else:
+            zc, zs = host(layer.z_codes[rows]), host(layer.z_scales[rows])
+            assert np.array_equal(zc, c_ref) and np.array_equal(zs, s_ref)
+            got = oracle.dequant_nvfp4_act(zc, zs)
+        assert np.array_equal(got, want)
+        return got
+    return bf16_to_f64(zb)
+
+
 def check_layer(w, T, W, fmt, act_mode, sample, layer_idx=0, residual=None, x=None, algo=moe.MOE_ALGO_AUTO,
-                dev_weights=None, cache=None):
+                dev_weights=None, cache=None, a_mode="dequant"):
     s = w.shape
-    say(f"layer {w.name} T={T} fmt={fmt} act={act_mode} layer={layer_idx} algo={algo}")
+    say(f"layer {w.name} T={T} fmt={fmt} act={act_mode} a_mode={a_mode} layer={layer_idx} algo={algo}")
     x = synth.activations(w, T, layer_idx) if x is None else x
     l = synth.logits(w, T, layer_idx)
     bias = synth.correction_bias(w, layer_idx)
     dw = upload_weights(W, fmt) if dev_weights is None else dev_weights
     layer = moe.MoELayer(dw, s.num_experts, s.n_group, s.topk_group, s.top_k, s.routed_scaling_factor, T,
-                         act_mode=act_mode, keep_z_bf16=True)
+                         act_mode=act_mode, keep_z_bf16=True, a_mode=a_mode)
     y = layer.forward(dev_bf16(x), dev_f32(l), None if bias is None else dev_f32(bias),
                       None if residual is None else dev_bf16(residual), algo=algo)
     torch.cuda.synchronize()
@@ -97,24 +125,22 @@ def check_layer(w, T, W, fmt, act_mode, sample, layer_idx=0, residual=None, x=No
         for j in range(s.top_k):
             e = int(ids[t, j])
             wd = cache(e)[2]
-            if act_mode == "nvfp4":
-                zc = host(layer.z_codes[rows[i * s.top_k + j]])[None, :]
-                zs = host(layer.z_scales[rows[i * s.top_k + j]])[None, :]
-                # the GPU's NVFP4 z is exactly the oracle's quantisation of the GPU's bf16 z
-                c_ref, s_ref = oracle.quantize_nvfp4(z_gpu[i, j][None, :], 1.0)
-                assert np.array_equal(zc, c_ref) and np.array_equal(zs, s_ref)
-                a = oracle.dequant_nvfp4_act(zc, zs)[0]
-            else:
-                a = bf16_to_f64(z_gpu[i, j])
+            r = rows[i * s.top_k + j]
+            # the GPU's quantised z is exactly the oracle's quantisation of the GPU's bf16 z
+            a = gpu_down_input(layer, slice(r, r + 1), z_gpu[i, j][None, :], act_mode, a_mode)[0]
             o_step[i, j] = a @ wd.T
     o_gpu = bf16_to_f64(o[rows].reshape(len(toks), s.top_k, -1))
     assert_close_rms(o_gpu, o_step, what="o (down out, step-wise)", ulp_rel=BF16_ULP)
-    assert_close_rms(o_gpu, ref.o, tol=5e-2, what="o (end-to-end)", ulp_rel=BF16_ULP)
+    # MXFP8 z: a one-ulp difference between the GPU's FP32-accumulated bf16 z and
+    # the oracle's float64 one can move an E4M3 code by one step (2^-3 relative),
+    # so end to end the W4A8 layer is reported; its bound holds step-wise
+    e2e_report = act_mode == "mxfp8"
+    assert_close_rms(o_gpu, ref.o, tol=5e-2, what="o (end-to-end)", ulp_rel=BF16_ULP, report_only=e2e_report)
     # combine from the GPU's own o; then end to end, against the float64 sums
     y_step = oracle.combine_f64(o_gpu, topw[toks].astype(np.float64), None if residual is None else residual[toks])
     assert_close_rms(bf16_to_f64(yb[toks]), y_step, what="y (step-wise, literal)")
-    assert_close_rms(bf16_to_f64(yb[toks]), ref.y_f64, what="y (end-to-end, literal)")
-    info = dict(layer=layer, x=x, z=z, o=o, ids=ids, offsets=off, sorted_slots=ss, act_mode=act_mode)
+    assert_close_rms(bf16_to_f64(yb[toks]), ref.y_f64, what="y (end-to-end, literal)", report_only=e2e_report)
+    info = dict(layer=layer, x=x, z=z, o=o, ids=ids, offsets=off, sorted_slots=ss, act_mode=act_mode, a_mode=a_mode)
     return yb, cache, info
 
 
@@ -147,27 +173,16 @@ def check_whole_experts(info, cache, top_k, extra=()):
     say(f"  whole experts {sorted(pick)} (rows {[int(rows[e]) for e in sorted(pick)]}; "
         f"XCD-slice straddlers {straddle})")
     x, z, o, ss = info["x"], info["z"], info["o"], info["sorted_slots"]
-    w4a4 = info["act_mode"] == "nvfp4"
     layer = info["layer"]
     for e in sorted(pick):
         r0, r1 = int(off[e]), int(off[e + 1])
         wg, wu, wd = cache(e)
         src = x[ss[r0:r1] // top_k]
-        if w4a4:
-            xc, xs = oracle.quantize_nvfp4(src, 1.0)
-            a = oracle.dequant_nvfp4_act(xc, xs)
-        else:
-            a = bf16_to_f64(src)
+        a = oracle.layer._act_values(src, info["act_mode"], 1.0)
         zref = bf16_to_f64(oracle.round_to_bf16_bits(oracle.silu(a @ wg.T) * (a @ wu.T)))
         zg = z[r0:r1]
         assert_close_rms(bf16_to_f64(zg), zref, what=f"z expert {e} ({r1 - r0} rows)", ulp_rel=BF16_ULP)
-        if w4a4:
-            zc, zs = host(layer.z_codes[r0:r1]), host(layer.z_scales[r0:r1])
-            c_ref, s_ref = oracle.quantize_nvfp4(zg, 1.0)
-            assert np.array_equal(zc, c_ref) and np.array_equal(zs, s_ref)
-            za = oracle.dequant_nvfp4_act(zc, zs)
-        else:
-            za = bf16_to_f64(zg)
+        za = gpu_down_input(layer, slice(r0, r1), zg, info["act_mode"], info["a_mode"])
         assert_close_rms(bf16_to_f64(o[r0:r1]), za @ wd.T, what=f"o expert {e}", ulp_rel=BF16_ULP)
 
 
@@ -381,4 +396,45 @@ def test_reap50_two_layers():
     del W1, info, cache
     W2 = synth.expert_weights(w, 1)
     _, cache, info = check_layer(w, T, W2, "mx", "bf16", sample, layer_idx=1, residual=y1, x=y1)
+    check_whole_experts(info, cache, w.shape.top_k)
+
+
+# ------------------------------------------- block-scaled MFMA layer modes
+def test_tiny_layer_scaled_modes():
+    """The tiny layer with W4A8 (MXFP8 activations) and with W4A4 on the
+    block-scaled MFMA (NVFP4 planes), every token, against the oracle."""
+    w = synth.WORKLOADS["tiny"]
+    W = synth.expert_weights(w)
+    check_layer(w, 32, W, "mx", "mxfp8", None)
+    nv = {}
+    for name in ("gate", "up", "down"):
+        sc, g, _ = oracle.transcode_mx_to_nv(W[name][1], W[name][0])
+        nv[name] = (W[name][0], sc, g)
+    dw = moe.LayerWeights(*(moe.Weights(dev_u8(nv[n][0]), dev_u8(nv[n][1]), dev_f32(nv[n][2]), scales_pow2=True,
+                                        mx_exact=True) for n in ("gate", "up", "down")))
+    check_layer(w, 32, nv, "nv", "nvfp4", None, dev_weights=dw, a_mode="planes")
+
+
+def test_prefill_layer_w4a8():
+    """W4A8 on the prefill workload (8192 tokens, biased routing): sampled tokens
+    end to end, whole experts step-wise."""
+    w = synth.WORKLOADS["prefill"]
+    W = synth.expert_weights(w)
+    _, cache, info = check_layer(w, 8192, W, "mx", "mxfp8", [0, 4097, 8191],
+                                 dev_weights=tiled(upload_weights(W, "mx")))
+    check_whole_experts(info, cache, w.shape.top_k)
+
+
+def test_w4a4_layer_planes():
+    """W4A4 (4096 tokens, NVFP4 transcoded weights) on the block-scaled MFMA."""
+    w = synth.WORKLOADS["w4a4"]
+    W = synth.expert_weights(w)
+    nv = {}
+    for name in ("gate", "up", "down"):
+        sc, g, _ = oracle.transcode_mx_to_nv(W[name][1], W[name][0])
+        nv[name] = (W[name][0], sc, g)
+    dw = moe.LayerWeights(*(moe.tile_weights(moe.Weights(dev_u8(nv[n][0]), dev_u8(nv[n][1]), dev_f32(nv[n][2]),
+                                                         scales_pow2=True, mx_exact=True))
+                            for n in ("gate", "up", "down")))
+    _, cache, info = check_layer(w, 4096, nv, "nv", "nvfp4", [1, 2048, 4095], dev_weights=dw, a_mode="planes")
     check_whole_experts(info, cache, w.shape.top_k)
