@@ -44,7 +44,33 @@ def _order_desc(values: np.ndarray) -> np.ndarray:
 def route(logits: np.ndarray, bias: Optional[np.ndarray], n_group: int, topk_group: int,
           top_k: int, routed_scaling_factor: float, norm_topk_prob: bool = True,
           group_score: str = "top2") -> RouteResult:
+    """Routing from FP32 logits (the router's output as stored)."""
     l = np.asarray(logits, dtype=np.float32).astype(np.float64)
+    return route_f64(l, bias, n_group, topk_group, top_k, routed_scaling_factor, norm_topk_prob, group_score)
+
+
+def router_logits(x_bits: np.ndarray, gate_weight: np.ndarray) -> np.ndarray:
+    """The router's matmul in float64: logits[t, e] = sum_k x[t, k] W[e, k] for
+    bf16 hidden states x and the FP32 router weight W [E, H] ([GGUF]
+    "Quantization targets": routers stay F32).  Every product of a bf16 and an
+    FP32 value is exact in float64; only the sum rounds."""
+    from .formats import bf16_value
+    return bf16_value(x_bits) @ np.asarray(gate_weight, np.float32).astype(np.float64).T
+
+
+def route_hidden(x_bits: np.ndarray, gate_weight: np.ndarray, bias: Optional[np.ndarray], n_group: int,
+                 topk_group: int, top_k: int, routed_scaling_factor: float, norm_topk_prob: bool = True):
+    """[PRO6000] "What makes it fast": the router's matmul and the top-k in one
+    step.  Reading: the float64 logits of router_logits feed the selection
+    directly (no rounding to FP32 in between).  Returns (RouteResult, logits)."""
+    l = router_logits(x_bits, gate_weight)
+    return route_f64(l, bias, n_group, topk_group, top_k, routed_scaling_factor, norm_topk_prob), l
+
+
+def route_f64(l: np.ndarray, bias: Optional[np.ndarray], n_group: int, topk_group: int,
+              top_k: int, routed_scaling_factor: float, norm_topk_prob: bool = True,
+              group_score: str = "top2") -> RouteResult:
+    """Routing from float64 logits l [T, E] (the steps of the module docstring)."""
     T, E = l.shape
     gs = E // n_group
     s = 1.0 / (1.0 + np.exp(-l))

@@ -22,13 +22,16 @@ Shapes follow the pages:
 Recipe (every tensor): numpy ``default_rng(SeedSequence([2026, workload id,
 layer, tensor id, tokens]))``; tensor ids: 0 logits, 1 correction bias, 2 x,
 3/4 gate codes/exponents, 5/6 up, 7/8 down, 9 synthetic down-proj input,
-10 outlier positions, 11 Zipf expert ranks.
+10 outlier positions, 11 Zipf expert ranks, 12 router weight.
   * codes: uniform random bytes (both nibbles uniform over all 16 E2M1 codes,
     including -0);
   * E8M0 scale bytes: uniform in {119..125}, i.e. 2^-8 .. 2^-2;
   * router logits: float32 N(0,1); REAP-50 shape adds ln p_r(e) with
     p_r proportional to r^-1.1 over a seeded rank permutation r(e);
   * correction bias: float32 N(0, 0.5) for the prefill shape, absent elsewhere;
+  * router weight (the FP32 gate.weight [E, hidden] for the fused router):
+    float32 N(0, 1/hidden), so that its logits on N(0,1) activations are
+    about N(0,1), like the synthetic logits;
   * activations: N(0,1) rounded to bfloat16 (round-to-nearest-even, done by
     torch's dtype conversion).
 """
@@ -44,6 +47,7 @@ SEED_ROOT = 2026
 T_LOGITS, T_BIAS, T_X = 0, 1, 2
 T_GATE_CODES, T_GATE_EXP, T_UP_CODES, T_UP_EXP, T_DOWN_CODES, T_DOWN_EXP = 3, 4, 5, 6, 7, 8
 T_ZSYN, T_OUTLIER_POS, T_ZIPF = 9, 10, 11
+T_ROUTER_W = 12
 
 E8M0_LO, E8M0_HI = 119, 125          # inclusive: 2^-8 .. 2^-2
 OUTLIER_AMAX = (2960.0, 18560.0, 311296.0)
@@ -115,6 +119,13 @@ def logits(w: Workload, T: int, layer: int = 0) -> np.ndarray:
         p /= p.sum()
         out = out + np.log(p)[None, :]
     return out.astype(np.float32)
+
+
+def router_weight(w: Workload, layer: int = 0) -> np.ndarray:
+    """FP32 router weight [E, hidden], N(0, 1/hidden)."""
+    g = rng(w.wid, layer, T_ROUTER_W)
+    H = w.shape.hidden
+    return (g.standard_normal((w.shape.num_experts, H)) / np.sqrt(H)).astype(np.float32)
 
 
 def correction_bias(w: Workload, layer: int = 0) -> Optional[np.ndarray]:

@@ -177,3 +177,44 @@ def test_near_tie_flag_on_constructed_gaps(gap_expert, gap_group, flag):
     assert sorted(r.ids[0][:7].tolist()) == [0, 1, 8, 9, 16, 17, 24]
     assert r.ids[0][7] == 2
     assert sorted({int(e) // 8 for e in r.ids[0]}) == [0, 1, 2, 3]
+
+
+# ------------------------------------------------ router matmul (fused router)
+def test_router_logits_within_float64_sum_bound():
+    """The float64 router matmul against exact rational dot products: every
+    product bf16 x FP32 is exact, so the only error is the float64 summation,
+    bounded by (H - 1) 2^-53 sum_k |x_k W_ek|."""
+    from fractions import Fraction
+    from synth import router_weight
+    w = WORKLOADS["decode"]
+    W = router_weight(w)[:6]
+    x = random_bf16_bits(7, (3, W.shape[1]))
+    l = oracle.router_logits(x, W)
+    xv = oracle.bf16_value(x)
+    H = W.shape[1]
+    for t in range(3):
+        for e in range(6):
+            exact = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(xv[t], W[e].astype(np.float64)))
+            bound = (H - 1) * 2.0 ** -53 * float(np.sum(np.abs(xv[t] * W[e].astype(np.float64))))
+            assert abs(Fraction(l[t, e]) - exact) <= Fraction(bound)
+
+
+def test_route_hidden_exhaustive_tiny():
+    """Routing from the float64 router logits agrees with exhaustive enumeration
+    of the group and expert subsets (the brute force of the FP32-logit pin, fed
+    the same float64 logits)."""
+    from synth import router_weight
+    w = WORKLOADS["tiny"]
+    s = w.shape
+    x = random_bf16_bits(8, (16, s.hidden))
+    W = router_weight(w)
+    r, l = oracle.route_hidden(x, W, None, s.n_group, s.topk_group, s.top_k, s.routed_scaling_factor)
+    for t in range(16):
+        ids, wts = _brute_force_tiny(l[t], None, s.n_group, s.topk_group, s.top_k, s.routed_scaling_factor)
+        assert list(r.ids[t]) == ids
+        np.testing.assert_allclose(r.weights[t], wts, rtol=1e-12)
+
+
+def random_bf16_bits(seed, shape):
+    from synth import random_bf16
+    return random_bf16(seed, shape)
