@@ -48,8 +48,8 @@ struct PfShape {
   static constexpr int WN = 8 / (BM / 64);
   static constexpr int AStage = BM * kPfBK * 2;            // bf16 tokens
   static constexpr int WStage = BN * kPfBK / 2;            // FP4 codes
-  static constexpr int SStage = BN * 8;                    // scales (MX uses half)
-  static constexpr int Stage = AStage + WStage + SStage;
+  static constexpr int SStage = BN * 8;                    // scales (MX uses half), a stage of their own
+  static constexpr int Stage = AStage + WStage;
 };
 // 128 x 256: the NVFP4-token kernel, and N not a multiple of 512 (256 SwiGLU)
 using PfTall = PfShape<128, 256>;
@@ -58,11 +58,19 @@ using PfTall = PfShape<128, 256>;
 using PfWide = PfShape<64, 512>;
 constexpr int kPfStageMax = PfWide::Stage > PfTall::Stage ? PfWide::Stage : PfTall::Stage;
 
+constexpr int kPfSStageMax = PfWide::SStage > PfTall::SStage ? PfWide::SStage : PfTall::SStage;
+
 // the three stages of the direct-to-LDS pipeline: separate objects, so the
-// compiler can tell a stage being read from the stages being filled
+// compiler can tell a stage being read from the stages being filled.  The
+// weight scales have stages of their own: inside the token / weight stages,
+// the first scale read of each step made the compiler wait for every load in
+// flight (the register weight path then drained the pipeline once per step).
 __shared__ __attribute__((aligned(16))) uint8_t pf_stage0[kPfStageMax];
 __shared__ __attribute__((aligned(16))) uint8_t pf_stage1[kPfStageMax];
 __shared__ __attribute__((aligned(16))) uint8_t pf_stage2[kPfStageMax];
+__shared__ __attribute__((aligned(16))) uint8_t pf_sstage0[kPfSStageMax];
+__shared__ __attribute__((aligned(16))) uint8_t pf_sstage1[kPfSStageMax];
+__shared__ __attribute__((aligned(16))) uint8_t pf_sstage2[kPfSStageMax];
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -217,12 +225,11 @@ struct PfNoHook {
 // (li, lg) at 16 * (16 lg + li)) instead of swizzled rows.
 // WREG: the weight codes come in registers (wreg[g]) instead of the LDS stage.
 template <int NMAT, int WF, bool TL, typename SH, bool WREG = false, typename Hook = PfNoHook>
-__device__ __forceinline__ void pf_compute(const uint8_t* st, f32x4 (&acc)[4][4], int wm, int wn, int li, int lg,
-                                           Hook&& hook = Hook(), const u32x4* wreg = nullptr) {
+__device__ __forceinline__ void pf_compute(const uint8_t* st, const uint8_t* ss, f32x4 (&acc)[4][4], int wm, int wn,
+                                           int li, int lg, Hook&& hook = Hook(), const u32x4* wreg = nullptr) {
   constexpr bool W_NV = WF != 0;
   const uint8_t* sa = st;
   const uint8_t* sw = st + SH::AStage;
-  const uint8_t* ss = st + SH::AStage + SH::WStage;
   u32x4 wq[4];
   float s_lo[4], s_hi[4];
 #pragma unroll
@@ -310,11 +317,15 @@ template <int S>
 __device__ __forceinline__ uint8_t* pf_stage() {
   return S == 0 ? pf_stage0 : (S == 1 ? pf_stage1 : pf_stage2);
 }
+template <int S>
+__device__ __forceinline__ uint8_t* pf_sstage() {
+  return S == 0 ? pf_sstage0 : (S == 1 ? pf_sstage1 : pf_sstage2);
+}
 
 template <int NMAT, int WF, bool TL, typename SH>
 __global__ __launch_bounds__(kPfThreads) void gemm_prefill_dma_kernel(GemmArgs p) {
   constexpr bool W_NV = WF != 0;
-  static_assert(3 * SH::Stage + (kPfMaxE + 1) * 4 + kPfThreads / kWave * 4 <= 160 * 1024, "LDS");
+  static_assert(3 * (kPfStageMax + kPfSStageMax) + (kPfMaxE + 1) * 4 + kPfThreads / kWave * 4 <= 160 * 1024, "LDS");
   __shared__ int s_pref[kPfMaxE + 1];
   __shared__ int s_wc[kPfThreads / kWave];
   // direct-to-LDS loads per wave and step: tokens (1 KB = 4 rows each), weight
@@ -424,7 +435,7 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_dma_kernel(GemmArgs p
       } else {
         const int h = q - kA - kW;
         __builtin_amdgcn_global_load_lds((const void*)(s_base[h] + pf_scale_step<TL, W_NV>(kb) + s_off[h]),
-                                         (lds_void_t*)(st + SH::AStage + SH::WStage + (wv * kS + h) * 256), 4, 0, 0);
+                                         (lds_void_t*)(pf_sstage<S>() + (wv * kS + h) * 256), 4, 0, 0);
       }
     };
     auto issue = [&](auto S_tag, int kb) {
@@ -458,7 +469,7 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_dma_kernel(GemmArgs p
       // every wave computes, also on rows past the tile's end (their outputs
       // are not stored): a branch here made the compiler drain every load in
       // flight before each step's first LDS read, losing the two-step lead
-      pf_compute<NMAT, WF, TL, SH, WREG>(pf_stage<S>(), acc, wm, wn, li, lg, hook, wring[S]);
+      pf_compute<NMAT, WF, TL, SH, WREG>(pf_stage<S>(), pf_sstage<S>(), acc, wm, wn, li, lg, hook, wring[S]);
     };
 
     __syncthreads();                                                 // previous tile done with the stages
@@ -488,6 +499,9 @@ struct PfRegs {
   u32x4 w[2];              // 2 weight-code chunks
   uint32_t s;              // one dword of weight scales
 };
+
+// one register-fed stage: token and weight codes, then the weight scales
+constexpr int kPfNvStage = PfTall::Stage + PfTall::SStage;
 
 template <int NMAT, int WF, bool TL>
 __global__ __launch_bounds__(kPfThreads) void gemm_prefill_nv_kernel(GemmArgs p) {
@@ -568,7 +582,7 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_nv_kernel(GemmArgs p)
     auto store = [&](const PfRegs& R, uint8_t* st) {
       uint8_t* sa = st;
       uint8_t* sw = st + PfTall::AStage;
-      uint8_t* ss = st + PfTall::AStage + PfTall::WStage;
+      uint8_t* ss = st + PfTall::Stage;
       const int row = tid >> 2, c = tid & 3;
       const float s_lo = e4m3_byte<0>(R.asc) * p.a_gscale, s_hi = e4m3_byte<1>(R.asc) * p.a_gscale;
 #pragma unroll
@@ -590,7 +604,7 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_nv_kernel(GemmArgs p)
       for (int t = 0; t < 4; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     uint8_t* st0 = lds;
-    uint8_t* st1 = lds + PfTall::Stage;
+    uint8_t* st1 = lds + kPfNvStage;
     PfRegs R0, R1;
     __syncthreads();                                                 // previous tile done with LDS
     fetch(R0, 0);
@@ -603,13 +617,13 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_nv_kernel(GemmArgs p)
     for (int kb = 0; kb < nk; kb += 2) {
       fetch(R0, min(kb + 2, nk - 1));
       __builtin_amdgcn_sched_barrier(0);
-      if (active) pf_compute<NMAT, WF, TL, PfTall>(st0, acc, wm, wn, li, lg);
+      if (active) pf_compute<NMAT, WF, TL, PfTall>(st0, st0 + PfTall::Stage, acc, wm, wn, li, lg);
       __builtin_amdgcn_sched_barrier(0);
       store(R1, st1);                                                // step kb + 1
       __syncthreads();
       fetch(R1, min(kb + 3, nk - 1));
       __builtin_amdgcn_sched_barrier(0);
-      if (active) pf_compute<NMAT, WF, TL, PfTall>(st1, acc, wm, wn, li, lg);
+      if (active) pf_compute<NMAT, WF, TL, PfTall>(st1, st1 + PfTall::Stage, acc, wm, wn, li, lg);
       __builtin_amdgcn_sched_barrier(0);
       store(R0, st0);                                                // step kb + 2
       __syncthreads();
@@ -627,10 +641,10 @@ static void launch_prefill_one(const GemmArgs& a, hipStream_t stream) {
     auto kern = gemm_prefill_nv_kernel<NMAT, WF, TL>;
     static bool attr_set = false;
     if (!attr_set) {
-      (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * PfTall::Stage);
+      (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kPfNvStage);
       attr_set = true;
     }
-    hipLaunchKernelGGL(kern, dim3(device_cus()), dim3(kPfThreads), 2 * PfTall::Stage, stream, a);
+    hipLaunchKernelGGL(kern, dim3(device_cus()), dim3(kPfThreads), 2 * kPfNvStage, stream, a);
   } else if (a.N % (PfWide::BN / NMAT) == 0) {      // bf16 tokens: 64 x 512 tiles where N allows
     hipLaunchKernelGGL((gemm_prefill_dma_kernel<NMAT, WF, TL, PfWide>), dim3(device_cus()), dim3(kPfThreads), 0, stream, a);
   } else {

@@ -47,7 +47,7 @@ struct SxShape {
   static constexpr int TSRow = PL ? 8 : 4;             // token scale bytes per row and step
   static constexpr int TSStage = BM * TSRow;
   static constexpr int WSStage = BN * 8;               // weight scale bytes (MX uses half)
-  static constexpr int Stage = AStage + TSStage + WSStage;
+  static constexpr int Stage = AStage + TSStage;         // token stage (weight scales: sw_stage)
   static constexpr int NH = PL ? 2 : 1;                // MFMA K-chunks per step of 128 values
 };
 constexpr int kSxStageMax = SxShape<true>::Stage;
@@ -59,6 +59,18 @@ __shared__ __attribute__((aligned(16))) uint8_t sx_stage2[kSxStageMax];
 template <int S>
 __device__ __forceinline__ uint8_t* sx_stage() {
   return S == 0 ? sx_stage0 : (S == 1 ? sx_stage1 : sx_stage2);
+}
+// Weight scales have stages of their own: objects separate from the token
+// stages let the compiler see that a weight-scale read of one stage does not
+// depend on the direct-to-LDS loads in flight into the others (with the scales
+// inside the token stages it waited for every load in flight before the first
+// scale read of each step).
+__shared__ __attribute__((aligned(16))) uint8_t sw_stage0[SxShape<true>::WSStage];
+__shared__ __attribute__((aligned(16))) uint8_t sw_stage1[SxShape<true>::WSStage];
+__shared__ __attribute__((aligned(16))) uint8_t sw_stage2[SxShape<true>::WSStage];
+template <int S>
+__device__ __forceinline__ uint8_t* sw_stage() {
+  return S == 0 ? sw_stage0 : (S == 1 ? sw_stage1 : sw_stage2);
 }
 
 // Token stage: 16-byte chunk c of row r sits at slot sx_swz(r, c) of the row
@@ -86,12 +98,11 @@ __device__ __forceinline__ int nv_pow2_e8m0(uint32_t byte, float gmul) {
 // One K step (128 values) from an LDS stage: 4 weight groups x 4 token groups
 // of 16 x 16, NH MFMA K-chunks each.  hook(s) runs before slot s's MFMAs.
 template <int NMAT, bool PL, bool W_NV, typename Hook>
-__device__ __forceinline__ void sx_compute(const uint8_t* st, f32x4 (&acc)[4][4], int wn, int li, int lg,
+__device__ __forceinline__ void sx_compute(const uint8_t* st, const uint8_t* sws, f32x4 (&acc)[4][4], int wn, int li, int lg,
                                            const u32x4* wreg, const float* gmul, Hook&& hook) {
   using SH = SxShape<PL>;
   const uint8_t* sa = st;
   const uint8_t* sts = st + SH::AStage;
-  const uint8_t* sws = st + SH::AStage + SH::TSStage;
 #pragma unroll
   for (int h = 0; h < SH::NH; ++h) {
     int wsc[4];
@@ -201,7 +212,7 @@ template <int NMAT, bool PL, bool TL, bool W_NV>
 __global__ __launch_bounds__(kPfThreads) void gemm_scaled_kernel(GemmArgs p) {
   using SH = SxShape<PL>;
   using WL = WeightLane<TL, W_NV>;
-  static_assert(3 * kSxStageMax + (kPfMaxE + 1) * 4 + kPfThreads / kWave * 4 <= 160 * 1024, "LDS");
+  static_assert(3 * (kSxStageMax + SH::WSStage) + (kPfMaxE + 1) * 4 + kPfThreads / kWave * 4 <= 160 * 1024, "LDS");
   __shared__ int s_pref[kPfMaxE + 1];
   __shared__ int s_wc[kPfThreads / kWave];
   // loads per wave and step: token codes (1 KB each), weight codes into
@@ -314,8 +325,7 @@ __global__ __launch_bounds__(kPfThreads) void gemm_scaled_kernel(GemmArgs p) {
       } else if (q < kW + kA + kS) {
         const int h = q - kW - kA;
         __builtin_amdgcn_global_load_lds((const void*)(s_base[h] + pf_scale_step<TL, W_NV>(kb) + s_off[h]),
-                                         (lds_void_t*)(st + SH::AStage + SH::TSStage + (wv * kS + h) * 256), 4, 0,
-                                         0);
+                                         (lds_void_t*)(sw_stage<S>() + (wv * kS + h) * 256), 4, 0, 0);
       } else {
         __builtin_amdgcn_global_load_lds((const void*)(p.a_scales + (int64_t)kb * SH::TSRow + ts_off),
                                          (lds_void_t*)(st + SH::AStage + ts_half * 256), 4, 0, 0);
@@ -347,7 +357,7 @@ __global__ __launch_bounds__(kPfThreads) void gemm_scaled_kernel(GemmArgs p) {
         if (2 * s < kDma) issue_one(SN, kn, 2 * s);
         if (2 * s + 1 < kDma) issue_one(SN, kn, 2 * s + 1);
       };
-      sx_compute<NMAT, PL, W_NV>(sx_stage<S>(), acc, wn, li, lg, wring[S], gmul, hook);
+      sx_compute<NMAT, PL, W_NV>(sx_stage<S>(), sw_stage<S>(), acc, wn, li, lg, wring[S], gmul, hook);
     };
 
     __syncthreads();                                             // previous tile done with the stages
