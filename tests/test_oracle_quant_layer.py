@@ -311,3 +311,37 @@ def test_mxfp8_brute_force_nearest():
                 want = best[1]
             want |= 0x80 if np.signbit(x[i, j]) else 0
             assert codes[i, j] == want, (i, j, x[i, j], codes[i, j], want)
+
+
+# ----------------------------------------------------------- REAP saliency
+def test_saliency_worked_example():
+    """Two tokens, top-2 of 3 experts, outputs with known norms (3-4-5 rows):
+    S_0 = (0.5 * 5 + 0.25 * 13) / 2, S_1 = 0.5 * 10, S_2 = 0.75 * 13, and S_j
+    is unchanged when the same batch is accumulated twice."""
+    o = np.zeros((2, 2, 4))
+    o[0, 0, :2] = [3, 4]          # token 0 -> expert 0, norm 5
+    o[0, 1, :2] = [6, 8]          # token 0 -> expert 1, norm 10
+    o[1, 0, 1:4] = [3, 4, 12]     # token 1 -> expert 2, norm 13
+    o[1, 1, 1:4] = [3, 4, 12]     # token 1 -> expert 0, norm 13
+    ids = np.array([[0, 1], [2, 0]])
+    g = np.array([[0.5, 0.5], [0.75, 0.25]])
+    sums, counts = oracle.saliency_accumulate(o, g, ids, 3)
+    np.testing.assert_array_equal(counts, [2, 1, 1])
+    np.testing.assert_allclose(oracle.saliency(sums, counts), [(2.5 + 3.25) / 2, 5.0, 9.75], rtol=1e-15)
+    sums2, counts2 = oracle.saliency_accumulate(o, g, ids, 3, sums.copy(), counts.copy())
+    np.testing.assert_allclose(oracle.saliency(sums2, counts2), oracle.saliency(sums, counts), rtol=1e-15)
+
+
+def test_saliency_equal_outputs_closed_form():
+    """Every expert output equal to v: S_j = mean of g over j's tokens x ||v||;
+    an expert no token reached has no saliency (NaN)."""
+    rng = np.random.default_rng(3)
+    T, k, E, H = 50, 4, 9, 16
+    v = rng.standard_normal(H)
+    ids = np.stack([rng.permutation(E - 1)[:k] for _ in range(T)])        # expert E-1 never routed
+    g = rng.uniform(0.1, 1.0, (T, k))
+    o = np.broadcast_to(v, (T, k, H))
+    S = oracle.saliency(*oracle.saliency_accumulate(o, g, ids, E))
+    for e in range(E - 1):
+        np.testing.assert_allclose(S[e], g[ids == e].mean() * np.linalg.norm(v), rtol=1e-13)
+    assert np.isnan(S[E - 1])
