@@ -27,11 +27,12 @@ from .permute import permute
 from .quant import quantize_nvfp4, dequant_nvfp4_act, quantize_mxfp8, dequant_mxfp8
 from .layer import silu, expert_ffn, combine, combine_f64, moe_layer, LayerResult
 from .saliency import saliency_accumulate, saliency
+from .compact import compact_mx, dequant_compact
 
 __all__ = [
     "E2M1_MAGNITUDES", "e2m1_value", "e8m0_value", "e4m3_value", "round_to_e4m3",
     "round_to_e2m1_magnitude", "bf16_value", "round_to_bf16_bits", "unpack_codes",
     "dequant_mx", "dequant_nv", "transcode_mx_to_nv", "route", "route_f64", "route_hidden", "router_logits", "RouteResult", "permute",
     "quantize_nvfp4", "dequant_nvfp4_act", "quantize_mxfp8", "dequant_mxfp8", "silu", "expert_ffn", "combine", "combine_f64", "moe_layer",
-    "LayerResult", "saliency_accumulate", "saliency",
+    "LayerResult", "saliency_accumulate", "saliency", "compact_mx", "dequant_compact",
 ]

@@ -99,3 +99,42 @@ def test_transcode_block_count_matches_pages():
     _, _, cnt = oracle.transcode_mx_to_nv(mx, packed)
     assert cnt["blocks"] * c["expert_matrices"] == c["expert_scale_blocks"]
     assert c["all_zero_blocks"] == 0 and c["rerounded_blocks"] == 0
+
+
+# ------------------------------------------------ compact storage (4.125 b/w)
+def test_compact_is_4p125_bits_and_lossless_on_model_shaped_data():
+    """The compact encoding of model-shaped MXFP4 weights takes 4.125 bits per
+    weight (the page's figure) and gives back exactly the MXFP4 values."""
+    from synth import WORKLOADS, expert_weights
+    W = expert_weights(WORKLOADS["decode"], experts=[0, 1])
+    for name in ("gate", "down"):
+        packed, mx = W[name]
+        c4, base, cnt = oracle.compact_mx(mx, packed)
+        assert cnt["rerounded"] == 0 and cnt["nan"] == 0 and cnt["blocks"] == mx.size
+        n_vals = packed.size * 2
+        assert (packed.nbytes + c4.nbytes) * 8 / n_vals == 4.125
+        for e in range(2):
+            assert np.array_equal(oracle.dequant_compact(packed[e], c4[e], base[e]),
+                                  oracle.dequant_mx(packed[e], mx[e]))
+
+
+def test_compact_edge_blocks():
+    """Span 15 below the largest exponent is exact; span 16 is re-rounded unless
+    the block is all zero; NaN has no code."""
+    from synth import random_mx_small
+    packed, mx = random_mx_small(31, 3, 16, 256, lo=110, hi=125)   # span 15: every block exact
+    packed = packed.copy()
+    mx = mx.copy()
+    c4, base, cnt = oracle.compact_mx(mx, packed)
+    assert cnt["rerounded"] == 0 and cnt["zero_oor"] == 0
+    for e in range(3):
+        assert np.array_equal(oracle.dequant_compact(packed[e], c4[e], base[e]), oracle.dequant_mx(packed[e], mx[e]))
+    mx[1, 2, 3] = 109                      # 16 below the largest: not expressible
+    mx[1, 4, 0] = 100
+    packed[1, 4, 0:16] = 0x88              # ... but all -0 codes: exact
+    mx[2, 0, 1] = 255                      # NaN
+    c4, base, cnt = oracle.compact_mx(mx, packed)
+    assert cnt["rerounded"] == 1 and cnt["zero_oor"] == 1 and cnt["nan"] == 1
+    assert np.array_equal(oracle.dequant_compact(packed[0], c4[0], base[0]), oracle.dequant_mx(packed[0], mx[0]))
+    d = oracle.dequant_compact(packed[1], c4[1], base[1])
+    assert np.all(d[4, 0:32] == 0)
