@@ -34,6 +34,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP4_PEAK_TFLOPS = 10100.0      # MI355X dense fp4 MFMA
 MX_BYTES_PER_WEIGHT = 0.5 + 1.0 / 32.0
+MXC_BYTES_PER_WEIGHT = 0.5 + 0.5 / 32.0       # compact MXFP4: a 4-bit exponent code per 32 weights
 
 # HBM bytes per launch of the decode gate/up GEMM at 64 tokens, measured with
 # rocprofv3 --pmc (FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000, the factors a plain
@@ -84,26 +85,29 @@ def layer_for(moe, lw, shape, T, act_mode="bf16"):
                         shape.routed_scaling_factor, T, act_mode=act_mode)
 
 
-def time_steps(layers, inputs, steps, warmup, algo=0, ev_name="gate_up"):
+def time_steps(layers, inputs, steps, warmup, algo=0, ev_names=("gate_up", "down")):
     """Run warmup + timed steps, rotating over (layer, input) pairs.  Returns
-    (ms per step, mean gate/up launch ms over the timed steps)."""
+    (ms per step, {kernel: mean launch ms over the timed steps}); the launch
+    times come from HIP events recorded on the launching stream around the
+    gate/up and down GEMM launches."""
     import torch
     n = len(layers)
     for i in range(warmup):
         x, l, b, r = inputs[i % len(inputs)]
         layers[i % n].forward(x, l, b, r, algo=algo)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+          for k in ev_names}
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(steps):
         x, l, b, r = inputs[i % len(inputs)]
-        layers[i % n].forward(x, l, b, r, algo=algo, events={ev_name: ev[i]})
+        layers[i % n].forward(x, l, b, r, algo=algo, events={k: ev[k][i] for k in ev_names})
     end.record()
     torch.cuda.synchronize()
     total = start.elapsed_time(end)
-    k_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    k_ms = {k: float(np.mean([a.elapsed_time(b) for a, b in ev[k]])) for k in ev_names}
     return total / steps, k_ms
 
 
@@ -146,17 +150,17 @@ def distinct_experts(layer, T):
     return int(np.sum(np.diff(off) > 0))
 
 
-def gate_up_bytes(D, T, shape):
+def gate_up_bytes(D, T, shape, bpw=MX_BYTES_PER_WEIGHT):
     """Algorithmic HBM bytes of one gate/up launch: the routed experts' gate and
     up weights once, the token rows once, z written once."""
     H, I, k = shape.hidden, shape.inter, shape.top_k
-    w = D * 2 * I * H * MX_BYTES_PER_WEIGHT
+    w = D * 2 * I * H * bpw
     return w + T * H * 2 + T * k * I * 2
 
 
-def layer_bytes(D, T, shape):
+def layer_bytes(D, T, shape, bpw=MX_BYTES_PER_WEIGHT):
     H, I, k, E = shape.hidden, shape.inter, shape.top_k, shape.num_experts
-    return D * 3 * I * H * MX_BYTES_PER_WEIGHT + T * (2 * H + 4 * E + 64 + 2 * H)
+    return D * 3 * I * H * bpw + T * (2 * H + 4 * E + 64 + 2 * H)
 
 
 def cpu_model():
@@ -200,6 +204,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--row-major", action="store_true",
                     help="keep the weights in their row-major layout (default: tiled once before timing)")
+    ap.add_argument("--decode-tokens", type=int, default=64,
+                    help="batch of the decode line (64 is the headline; other values only for profiling)")
+    ap.add_argument("--workload", default="all", choices=["all"] + list(WORKLOAD_RUNNERS) + list(SWEEPS),
+                    help="run one extra workload alone and print its figures (for profiling)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes) and exit")
@@ -226,10 +234,14 @@ def main():
     import synth
 
     torch.cuda.init()
+    if args.workload != "all":
+        r = {**WORKLOAD_RUNNERS, **SWEEPS}[args.workload](moe, synth, args)
+        print(json.dumps({"workload_only": EXTRA_KEYS[args.workload], "result": r}), flush=True)
+        return
     wd = synth.WORKLOADS["decode"]
     s = wd.shape
     log(f"[bench] generating {args.rotate} decode weight sets")
-    Ws = [synth.expert_weights(wd, layer=i) for i in range(args.rotate)]
+    Ws = [host_weights(synth, "decode", i) for i in range(args.rotate)]
     lws = [make_weights(W) for W in Ws]
     torch.cuda.synchronize()
 
@@ -239,6 +251,7 @@ def main():
         inputs = [(dev_bf16(x), dev(l), None, None)]
         layers = [layer_for(moe, lw, s, T) for lw in lws]
         ms, k_ms = time_steps(layers, inputs, steps, warmup)
+        k_ms = k_ms["gate_up"]
         g_ms = graph_steps(layers, inputs, steps, warmup) if graph else None
         Ds = []
         for ly in layers:
@@ -247,9 +260,9 @@ def main():
         D = float(np.mean(Ds))
         return dict(T=T, ms=ms, gate_up_ms=k_ms, graph_ms=g_ms, D=D, x=x, l=l, layers=layers)
 
-    log("[bench] decode T=64 (headline)")
-    main_r = decode_line(64, args.steps, args.warmup, graph=True)
-    T = 64
+    T = args.decode_tokens
+    log(f"[bench] decode T={T} (headline)")
+    main_r = decode_line(T, args.steps, args.warmup, graph=True)
     step_ms = main_r["graph_ms"]            # the layer step replayed from a captured HIP graph
     tok_s = T / (step_ms / 1e3)
     gu_bytes = gate_up_bytes(main_r["D"], T, s)
@@ -272,7 +285,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "decode W4A16 MXFP4: 256 experts (8 groups, keep 4, top-8, scale 2.827), "
-                               "hidden 4096, expert intermediate 2048, 64 tokens, 4 rotated weight sets",
+                               f"hidden 4096, expert intermediate 2048, {T} tokens, 4 rotated weight sets",
                    "tokens": T, "experts": 256, "hidden": 4096, "intermediate": 2048, "top_k": 8,
                    "weights": "MXFP4, " + ("tiled layout" if TILED else "row-major"), "activations": "bf16",
                    "distinct_experts": main_r["D"]},
@@ -298,7 +311,8 @@ def main():
                                        "gate_up_hbm_frac": round(gate_up_bytes(r["D"], Tx, s) / (r["gate_up_ms"] / 1e3)
                                                                  / 1e9 / HBM_PEAK_GBS, 4)}
             del r
-        extras.update(prefill_lines(moe, synth, Ws[0], args))
+        for name, fn in WORKLOAD_RUNNERS.items():
+            extras[EXTRA_KEYS[name]] = fn(moe, synth, args)
     out["extras"] = extras
     if not args.no_cpu:
         log("[bench] CPU oracle baseline")
@@ -313,39 +327,66 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def prefill_lines(moe, synth, decode_W, args):
-    """MFMA-bound shapes: prefill (T=8192, biased routing), W4A4 (T=4096 on the
-    NVFP4 transcode of the decode weights) and REAP-50 (128 experts, 2 layers)."""
+_HOST_WEIGHTS = {}
+
+
+def host_weights(synth, name, layer=0):
+    """Seeded host weights of a workload, generated once per run."""
+    key = (name, layer)
+    if key not in _HOST_WEIGHTS:
+        _HOST_WEIGHTS[key] = synth.expert_weights(synth.WORKLOADS[name], layer)
+    return _HOST_WEIGHTS[key]
+
+
+FP8_PEAK_TFLOPS = 5000.0      # MI355X dense fp8 MFMA (an FP8 x FP4 block-scaled MFMA runs at this rate)
+FLOPS_PER_TOKEN = 402653184.0  # 8 experts x 6 x 4096 x 2048 per token and layer
+
+
+def _frac(T, ms, peak, layers=1):
+    return T * FLOPS_PER_TOKEN * layers / (ms / 1e3) / 1e12 / peak
+
+
+def _kernel_fracs(T, k_ms, peak):
+    """Algorithmic MFMA fraction of the gate/up (2/3 of the FLOPs) and down (1/3) launches."""
+    f = T * FLOPS_PER_TOKEN
+    return {"gate_up_ms": round(k_ms["gate_up"], 4), "down_ms": round(k_ms["down"], 4),
+            "gate_up_frac": round(f * 2 / 3 / (k_ms["gate_up"] / 1e3) / 1e12 / peak, 4),
+            "down_frac": round(f / 3 / (k_ms["down"] / 1e3) / 1e12 / peak, 4)}
+
+
+def run_prefill(moe, synth, args, act_mode="bf16"):
+    """Prefill shape, 8192 tokens, biased routing; W4A16 (bf16 MFMA) or W4A8
+    (MXFP8 activations, block-scaled FP8 x FP4 MFMA)."""
     import torch
-    res = {}
-    steps = max(5, min(args.steps, 20))
-    warm = 3
-
-    def mfma_frac(T, ms, layers=1):
-        flops = T * 402653184.0 * layers
-        return flops / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS
-
+    steps, warm = max(5, min(args.steps, 20)), 3
     wp = synth.WORKLOADS["prefill"]
-    log("[bench] prefill T=8192")
-    Wp = synth.expert_weights(wp)
-    lwp = make_weights(Wp)
-    del Wp
+    log(f"[bench] prefill T=8192 act={act_mode}")
+    lw = make_weights(host_weights(synth, "prefill"))
     T = 8192
-    x = dev_bf16(synth.activations(wp, T))
-    l = dev(synth.logits(wp, T))
-    b = dev(synth.correction_bias(wp))
-    ly = layer_for(moe, lwp, wp.shape, T)
+    x, l, b = dev_bf16(synth.activations(wp, T)), dev(synth.logits(wp, T)), dev(synth.correction_bias(wp))
+    ly = layer_for(moe, lw, wp.shape, T, act_mode=act_mode)
     ms, k_ms = time_steps([ly], [(x, l, b, None)], steps, warm)
-    res["prefill_T8192"] = {"tokens_per_s": round(T / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
-                            "mfma_frac_bf16": round(mfma_frac(T, ms), 4), "gate_up_ms": round(k_ms, 4)}
-    del ly, lwp
+    peak = BF16_PEAK_TFLOPS if act_mode == "bf16" else FP8_PEAK_TFLOPS
+    r = {"tokens_per_s": round(T / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
+         "mfma_frac_bf16": round(_frac(T, ms, BF16_PEAK_TFLOPS), 4)}
+    if act_mode != "bf16":
+        r["mfma_frac_fp8"] = round(_frac(T, ms, FP8_PEAK_TFLOPS), 4)
+    r.update(_kernel_fracs(T, k_ms, peak))
+    del ly, lw
     torch.cuda.empty_cache()
+    return r
 
-    log("[bench] W4A4 T=4096")
+
+def run_w4a4(moe, synth, args, a_mode="dequant"):
+    """NVFP4 W4A4, 4096 tokens on the exact NVFP4 transcode of the decode
+    weights; a_mode "dequant" (bf16 MFMA on the exact NVFP4 values) or
+    "planes" (block-scaled MFMA, FP4 weights native)."""
+    import torch
+    steps, warm = max(5, min(args.steps, 20)), 3
     ww = synth.WORKLOADS["w4a4"]
-    src = make_weights(decode_W, tiled=False)    # the transcode reads the row-major MXFP4 tensors
-    nvw = {}
-    tc_ms = []
+    log(f"[bench] W4A4 T=4096 a_mode={a_mode}")
+    src = make_weights(host_weights(synth, "w4a4"), tiled=False)    # the transcode reads the row-major tensors
+    nvw, tc_ms = {}, []
     for name in ("gate", "up", "down"):
         t = getattr(src, name)
         M, n, kb = t.scale.shape
@@ -360,24 +401,75 @@ def prefill_lines(moe, synth, decode_W, args):
         torch.cuda.synchronize()
         tc_ms.append(e0.elapsed_time(e1))
         assert int(cnt[2].item()) == 0
-        nvw[name] = moe.Weights(t.packed, sc, g, scales_pow2=True)    # the transcode's scales are powers of two
+        nvw[name] = moe.Weights(t.packed, sc, g, scales_pow2=True, mx_exact=True)   # an exact MX transcode
         if TILED:
             nvw[name] = moe.tile_weights(nvw[name])
     E = ww.shape.num_experts
     tc_bytes = 3 * E * 2048 * 4096 * (1 / 32 + 2 / 16)      # read E8M0, write 2x E4M3
     T = 4096
     lw4 = moe.LayerWeights(nvw["gate"], nvw["up"], nvw["down"])
-    ly = layer_for(moe, lw4, ww.shape, T, act_mode="nvfp4")
-    x = dev_bf16(synth.activations(ww, T))
-    l = dev(synth.logits(ww, T))
+    ly = moe.MoELayer(lw4, E, ww.shape.n_group, ww.shape.topk_group, ww.shape.top_k, ww.shape.routed_scaling_factor,
+                      T, act_mode="nvfp4", a_mode=a_mode)
+    x, l = dev_bf16(synth.activations(ww, T)), dev(synth.logits(ww, T))
     ms, k_ms = time_steps([ly], [(x, l, None, None)], steps, warm)
-    res["w4a4_T4096"] = {"tokens_per_s": round(T / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
-                         "mfma_frac_bf16": round(mfma_frac(T, ms), 4),
-                         "fp4_peak_frac": round(mfma_frac(T, ms) * BF16_PEAK_TFLOPS / FP4_PEAK_TFLOPS, 4),
-                         "transcode_GBs": round(tc_bytes / (sum(tc_ms) / 1e3) / 1e9, 1)}
+    r = {"tokens_per_s": round(T / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
+         "mfma_frac_bf16": round(_frac(T, ms, BF16_PEAK_TFLOPS), 4),
+         "fp4_peak_frac": round(_frac(T, ms, FP4_PEAK_TFLOPS), 4),
+         "transcode_GBs": round(tc_bytes / (sum(tc_ms) / 1e3) / 1e9, 1)}
+    r.update(_kernel_fracs(T, k_ms, BF16_PEAK_TFLOPS))
     del ly, lw4, nvw, src
     torch.cuda.empty_cache()
+    return r
 
+
+def run_outliers(moe, synth, args):
+    """Down projection alone on bf16 z [32768, 2048] N(0,1) with 0.1% outliers
+    of amax 2960 / 18560 / 311296, quantised to NVFP4 (saturating at 2688) and
+    multiplied on the exact NVFP4 values (bf16 MFMA)."""
+    import torch
+    ww = synth.WORKLOADS["w4a4"]
+    s = ww.shape
+    rows, E = 32768, s.num_experts
+    log("[bench] down projection with outliers")
+    Wd = synth.mx_matrix(2, 0, synth.T_DOWN_CODES, synth.T_DOWN_EXP, E, s.hidden, s.inter)
+    w = moe.Weights(dev(Wd[0]), dev(Wd[1]))
+    wt = moe.tile_weights(w) if TILED else w
+    offsets = dev(np.asarray(np.arange(E + 1) * (rows // E), dtype=np.int32))
+    out = torch.empty((rows, s.hidden), dtype=torch.bfloat16, device="cuda")
+    zc = torch.empty((rows, s.inter // 2), dtype=torch.uint8, device="cuda")
+    zs = torch.empty((rows, s.inter // 16), dtype=torch.uint8, device="cuda")
+    zdq = torch.empty((rows, s.inter), dtype=torch.bfloat16, device="cuda")
+    res = {}
+    for amax in synth.OUTLIER_AMAX:
+        z = dev_bf16(synth.down_inputs_with_outliers(rows, s.inter, amax))
+
+        def step():
+            moe.quantize_nvfp4(z, 1.0, zc, zs, dequant=zdq)
+            moe.grouped_gemm(zdq, wt, None, offsets, rows, out=out)
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = 10
+        e0.record()
+        for _ in range(n):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        flops = 2.0 * rows * s.hidden * s.inter
+        byts = E * s.hidden * s.inter * MX_BYTES_PER_WEIGHT + rows * s.inter * 2 * 2 + rows * s.hidden * 2
+        res[f"amax_{int(amax)}"] = {"ms": round(ms, 4), "TFLOPs": round(flops / (ms / 1e3) / 1e12, 1),
+                                    "mfma_frac_bf16": round(flops / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                                    "GBs": round(byts / (ms / 1e3) / 1e9, 1),
+                                    "saturated_max": float(zdq.float().abs().max().item())}
+        del z
+    return res
+
+
+def run_reap50(moe, synth, args):
+    import torch
+    steps, warm = max(5, min(args.steps, 20)), 3
     log("[bench] REAP-50 T=16384, 2 layers")
     wr = synth.WORKLOADS["reap50"]
     T = 16384
@@ -389,21 +481,145 @@ def prefill_lines(moe, synth, decode_W, args):
         h1 = lys[0].forward(h0, ls[0], None, h0)
         lys[1].forward(h1, ls[1], None, h1)
     torch.cuda.synchronize()
+    ev = {k: [] for k in ("gate_up", "down")}
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
-        h1 = lys[0].forward(h0, ls[0], None, h0)
-        lys[1].forward(h1, ls[1], None, h1)
+        evs = [{k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for k in ev}
+               for _ in range(2)]
+        h1 = lys[0].forward(h0, ls[0], None, h0, events=evs[0])
+        lys[1].forward(h1, ls[1], None, h1, events=evs[1])
+        for k in ev:
+            ev[k] += [evs[0][k], evs[1][k]]
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    off = lys[0].offsets.cpu().numpy()
-    loads = np.diff(off)
-    res["reap50_T16384_2layers"] = {"tokens_per_s_per_layer": round(2 * T / (ms / 1e3), 1),
-                                    "ms_per_step_2layers": round(ms, 4),
-                                    "mfma_frac_bf16": round(mfma_frac(T, ms, 2), 4),
-                                    "expert_load_max": int(loads.max()), "expert_load_median": float(np.median(loads))}
+    k_ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
+    loads = np.diff(lys[0].offsets.cpu().numpy())
+    r = {"tokens_per_s_per_layer": round(2 * T / (ms / 1e3), 1), "ms_per_step_2layers": round(ms, 4),
+         "mfma_frac_bf16": round(_frac(T, ms, BF16_PEAK_TFLOPS, 2), 4),
+         "expert_load_max": int(loads.max()), "expert_load_median": float(np.median(loads))}
+    r.update(_kernel_fracs(T, k_ms, BF16_PEAK_TFLOPS))
+    del lys, lws
+    torch.cuda.empty_cache()
+    return r
+
+
+def run_compact(moe, synth, args):
+    """The decode line (T = 1, 8, 64; 4 rotated weight sets, HIP-graph replay)
+    on the same weights in compact MXFP4 storage (4.125 bits per weight)."""
+    import torch
+    wd = synth.WORKLOADS["decode"]
+    s = wd.shape
+    log("[bench] compact MXFP4 decode")
+    lws = []
+    for i in range(args.rotate):
+        src = make_weights(host_weights(synth, "decode", i), tiled=False)
+        ws = []
+        for name in ("gate", "up", "down"):
+            w, cnt = moe.compact_weights(getattr(src, name))
+            assert int(cnt[2].item()) == 0 and int(cnt[3].item()) == 0     # lossless
+            ws.append(moe.tile_weights(w) if TILED else w)
+        lws.append(moe.LayerWeights(*ws))
+        del src
+    torch.cuda.synchronize()
+    res = {}
+    for T in (1, 8, 64):
+        x, l = dev_bf16(synth.activations(wd, T)), dev(synth.logits(wd, T))
+        inputs = [(x, l, None, None)]
+        layers = [layer_for(moe, lw, s, T) for lw in lws]
+        steps = max(args.steps, 50)
+        ms, k_ms = time_steps(layers, inputs, steps, args.warmup)
+        g_ms = graph_steps(layers, inputs, steps, args.warmup)
+        D = float(np.mean([distinct_experts(ly, T) for ly in layers]))
+        res[f"T{T}"] = {"hip_graph_ms_per_step": round(g_ms, 4), "hip_graph_tokens_per_s": round(T / (g_ms / 1e3), 1),
+                        "ms_per_step_eager": round(ms, 4), "distinct_experts": D,
+                        "layer_hbm_frac": round(layer_bytes(D, T, s, MXC_BYTES_PER_WEIGHT) / (g_ms / 1e3) / 1e9
+                                                / HBM_PEAK_GBS, 4),
+                        "gate_up_ms": round(k_ms["gate_up"], 5),
+                        "gate_up_hbm_frac": round(gate_up_bytes(D, T, s, MXC_BYTES_PER_WEIGHT) / (k_ms["gate_up"] / 1e3)
+                                                  / 1e9 / HBM_PEAK_GBS, 4)}
+        del layers
+    del lws
+    torch.cuda.empty_cache()
     return res
+
+
+def run_tsweep(moe, synth, args):
+    """Both GEMM kernels forced at each batch (decode weights, tiled): the
+    token counts where the MFMA-tiled kernel overtakes the weight-streaming one
+    (MOE_ALGO_AUTO switches at rows >= 32 E, i.e. 1024 tokens at 256 experts)."""
+    import torch
+    wd = synth.WORKLOADS["decode"]
+    s = wd.shape
+    lw = make_weights(host_weights(synth, "decode", 0))
+    res = {}
+    for T in (128, 256, 512, 768, 1024, 1536, 2048, 4096):
+        x, l = dev_bf16(synth.activations(wd, T)), dev(synth.logits(wd, T))
+        ly = layer_for(moe, lw, s, T)
+        row = {}
+        for name, algo in (("decode", moe.MOE_ALGO_DECODE), ("prefill", moe.MOE_ALGO_PREFILL)):
+            ms, k_ms = time_steps([ly], [(x, l, None, None)], 10, 3, algo=algo)
+            row[name] = {"layer_ms": round(ms, 4), "gate_up_ms": round(k_ms["gate_up"], 4),
+                         "down_ms": round(k_ms["down"], 4)}
+        log(f"[bench] T-sweep T={T}: decode {row['decode']['layer_ms']} ms, prefill {row['prefill']['layer_ms']} ms")
+        res[f"T{T}"] = row
+        del ly
+    del lw
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_router(moe, synth, args):
+    """Router matmul fused with the group top-k (moe_route_gemv) at decode
+    batches, against the top-k alone on given logits (moe_route) and a torch
+    FP32 matmul (the unfused router's matmul)."""
+    import torch
+    w = synth.WORKLOADS["decode"]
+    RW = dev(synth.router_weight(w))
+    res = {}
+    for T in (1, 8, 64):
+        log(f"[bench] fused router T={T}")
+        x, l = dev_bf16(synth.activations(w, T)), dev(synth.logits(w, T))
+        ws = torch.zeros(moe.route_gemv_workspace_bytes(T, 256), dtype=torch.uint8, device="cuda")
+        ids = torch.empty((T, 8), dtype=torch.int32, device="cuda")
+        wt = torch.empty((T, 8), dtype=torch.float32, device="cuda")
+
+        def us(f, n=100):
+            for _ in range(10):
+                f()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(n):
+                f()
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / n * 1000
+        res[f"T{T}"] = {
+            "route_gemv_us": round(us(lambda: moe.route_gemv(x, RW, None, 256, 8, 4, 8, 2.827, ws, ids=ids,
+                                                             weights=wt)), 2),
+            "route_only_us": round(us(lambda: moe.route(l, None, 256, 8, 4, 8, 2.827, ids=ids, weights=wt)), 2),
+            "torch_fp32_matmul_us": round(us(lambda: torch.matmul(x.float(), RW.t())), 2)}
+    return res
+
+
+WORKLOAD_RUNNERS = {
+    "prefill": lambda moe, synth, a: run_prefill(moe, synth, a, "bf16"),
+    "w4a8": lambda moe, synth, a: run_prefill(moe, synth, a, "mxfp8"),
+    "w4a4": lambda moe, synth, a: run_w4a4(moe, synth, a, "dequant"),
+    "w4a4_planes": lambda moe, synth, a: run_w4a4(moe, synth, a, "planes"),
+    "reap50": run_reap50,
+    "outliers": run_outliers,
+    "router": run_router,
+    "compact": run_compact,
+}
+# run only when asked for (--workload tsweep): a sweep for the kernel choice, not a bench line
+SWEEPS = {"tsweep": run_tsweep}
+EXTRA_KEYS = {"prefill": "prefill_T8192", "w4a8": "prefill_T8192_w4a8_mxfp8", "w4a4": "w4a4_T4096",
+              "w4a4_planes": "w4a4_T4096_planes", "reap50": "reap50_T16384_2layers",
+              "outliers": "down_proj_outliers_32768x2048", "router": "fused_router_decode",
+              "compact": "decode_compact_mxfp4_4p125", "tsweep": "gemm_kernel_choice_T_sweep"}
 
 
 if __name__ == "__main__":

@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoefp4.so")
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, 1, 2, 3, 4
-MOE_FP4_MX, MOE_FP4_NV = 0, 1
+MOE_FP4_MX, MOE_FP4_NV, MOE_FP4_MXC = 0, 1, 2
 MOE_FP4_SCALES_POW2, MOE_FP4_TILED, MOE_FP4_MX_EXACT = 1, 2, 4
 MOE_ACT_BF16, MOE_ACT_NVFP4, MOE_ACT_MXFP8, MOE_ACT_NVFP4_PLANES = 0, 1, 2, 3
 MOE_OUT_NVFP4, MOE_OUT_MXFP8, MOE_OUT_NVFP4_PLANES = 0, 1, 2
@@ -26,7 +26,8 @@ MOE_ALGO_AUTO, MOE_ALGO_DECODE, MOE_ALGO_PREFILL = 0, 1, 2
 
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_version", "moe_route", "moe_permute_workspace_bytes",
            "moe_permute", "moe_route_permute", "moe_fp4_grouped_gemm", "moe_combine", "fp4_transcode_mx_to_nv", "moe_quantize_nvfp4",
-           "moe_fp4_tile_weights", "moe_route_permute_noalloc", "moe_quantize_mxfp8", "moe_quantize_nvfp4_planes")
+           "moe_fp4_tile_weights", "moe_route_permute_noalloc", "moe_quantize_mxfp8", "moe_quantize_nvfp4_planes",
+           "moe_route_gemv_workspace_bytes", "moe_route_gemv", "moe_reap_saliency_accumulate", "moe_fp4_compact_mx")
 
 
 class RouteParams(ctypes.Structure):
@@ -49,7 +50,8 @@ class Act(ctypes.Structure):
 
 class Out(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
-                ("output_scale", ctypes.c_float), ("dequant", ctypes.c_void_p), ("format", ctypes.c_int32)]
+                ("output_scale", ctypes.c_float), ("dequant", ctypes.c_void_p), ("format", ctypes.c_int32),
+                ("row_sumsq", ctypes.c_void_p)]
 
 
 def _load() -> ctypes.CDLL:
@@ -82,6 +84,14 @@ def _load() -> ctypes.CDLL:
     lib.moe_quantize_nvfp4.argtypes = [vp, i64, i32, f32, vp, vp, vp, vp]
     lib.moe_route_permute_noalloc.restype = i32
     lib.moe_route_permute_noalloc.argtypes = [vp, vp, i64, ctypes.POINTER(RouteParams), vp, vp, vp, vp, vp, vp]
+    lib.moe_route_gemv_workspace_bytes.restype = sz
+    lib.moe_route_gemv_workspace_bytes.argtypes = [i64, i32]
+    lib.moe_route_gemv.restype = i32
+    lib.moe_route_gemv.argtypes = [vp, vp, vp, i64, i32, ctypes.POINTER(RouteParams), vp, vp, vp, sz, vp]
+    lib.moe_reap_saliency_accumulate.restype = i32
+    lib.moe_reap_saliency_accumulate.argtypes = [vp, i64, i32, vp, i32, vp, vp, vp, vp, vp]
+    lib.moe_fp4_compact_mx.restype = i32
+    lib.moe_fp4_compact_mx.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp, vp]
     lib.moe_quantize_mxfp8.restype = i32
     lib.moe_quantize_mxfp8.argtypes = [vp, i64, i32, vp, vp, vp]
     lib.moe_quantize_nvfp4_planes.restype = i32
@@ -132,6 +142,28 @@ def route(logits: torch.Tensor, bias: Optional[torch.Tensor], num_experts: int, 
     p = RouteParams(num_experts, n_group, topk_group, top_k, routed_scaling_factor, int(norm_topk_prob))
     _check(lib.moe_route(_ptr(logits), _ptr(bias), T, ctypes.byref(p), _ptr(ids), _ptr(weights), _stream(stream)),
            "moe_route")
+    return ids, weights
+
+
+def route_gemv_workspace_bytes(T: int, num_experts: int) -> int:
+    return int(lib.moe_route_gemv_workspace_bytes(T, num_experts))
+
+
+def route_gemv(x: torch.Tensor, gate_weight: torch.Tensor, bias: Optional[torch.Tensor], num_experts: int,
+               n_group: int, topk_group: int, top_k: int, routed_scaling_factor: float, workspace: torch.Tensor,
+               norm_topk_prob: bool = True, ids=None, weights=None, stream=None):
+    """Router matmul (bf16 x, FP32 gate_weight [E, hidden], float64 sums) and
+    group top-k in one launch.  ``workspace``: uint8 of at least
+    route_gemv_workspace_bytes(T, E), zeroed before its first use; after the
+    call its first T*E*8 bytes hold the float64 logits."""
+    _dev(x, "x")
+    _dev(gate_weight, "gate_weight")
+    T, H = x.shape
+    ids = torch.empty((T, top_k), dtype=torch.int32, device=x.device) if ids is None else ids
+    weights = torch.empty((T, top_k), dtype=torch.float32, device=x.device) if weights is None else weights
+    p = RouteParams(num_experts, n_group, topk_group, top_k, routed_scaling_factor, int(norm_topk_prob))
+    _check(lib.moe_route_gemv(_ptr(x), _ptr(gate_weight), _ptr(bias), T, H, ctypes.byref(p), _ptr(ids), _ptr(weights),
+                              _ptr(workspace), workspace.numel(), _stream(stream)), "moe_route_gemv")
     return ids, weights
 
 
@@ -200,16 +232,19 @@ def route_permute_noalloc(logits: torch.Tensor, bias: Optional[torch.Tensor], nu
 
 @dataclasses.dataclass
 class Weights:
-    """One stacked expert matrix [E, n, k] in MXFP4 or NVFP4 (device tensors)."""
+    """One stacked expert matrix [E, n, k] in MXFP4, NVFP4 or compact MXFP4 (device tensors)."""
     packed: torch.Tensor                  # u8 [E, n, k/2]
-    scale: torch.Tensor                   # u8 [E, n, k/32] (MX) | [E, n, k/16] (NV)
-    global_scale: Optional[torch.Tensor] = None   # f32 [E] (NV)
+    scale: torch.Tensor                   # u8 [E, n, k/32] (MX) | [E, n, k/16] (NV) | [E, n, k/64] (compact)
+    global_scale: Optional[torch.Tensor] = None   # f32 [E] (NV global; compact base 2^b)
     scales_pow2: bool = False             # NV: every scale byte is 0 or a power of two (a transcode)
     tiled: bool = False                   # codes and scales in the tiled layout (see tile_weights)
     mx_exact: bool = False                # NV: an exact MXFP4 transcode (E8M0 per 32 exists)
+    compact: bool = False                 # compact MXFP4 (see compact_mx): 4-bit exponent codes + base
 
     @property
     def format(self):
+        if self.compact:
+            return MOE_FP4_MXC
         return MOE_FP4_NV if self.global_scale is not None else MOE_FP4_MX
 
     def c(self) -> Fp4Weights:
@@ -229,7 +264,7 @@ def grouped_gemm(a: torch.Tensor, w0: Weights, w1: Optional[Weights], offsets: t
                  input_scale: float = 1.0, out: Optional[torch.Tensor] = None, out_codes: Optional[torch.Tensor] = None,
                  out_scales: Optional[torch.Tensor] = None, output_scale: float = 1.0, want_bf16: bool = True,
                  out_dequant: Optional[torch.Tensor] = None, algo: int = MOE_ALGO_AUTO, a_mode: Optional[str] = None,
-                 out_format: str = "nvfp4", stream=None):
+                 out_format: str = "nvfp4", row_sumsq: Optional[torch.Tensor] = None, stream=None):
     """A: bf16 [rows_src, k] (W4A16); NVFP4 codes u8 [rows_src, k/2] with ``a_scales`` (W4A4);
     ``a_mode="mxfp8"``: E4M3 codes [rows_src, k] + E8M0 [rows_src, k/32] (W4A8);
     ``a_mode="planes"``: NVFP4 planes [rows_src, 2k] + E8M0 [rows_src, k/16] (W4A4, block-scaled MFMA).
@@ -245,7 +280,8 @@ def grouped_gemm(a: torch.Tensor, w0: Weights, w1: Optional[Weights], offsets: t
               None if gather is None else gather.data_ptr(), int(gather_div), a.shape[0])
     o = Out(None if out is None else out.data_ptr(), None if out_codes is None else out_codes.data_ptr(),
             None if out_scales is None else out_scales.data_ptr(), float(output_scale),
-            None if out_dequant is None else out_dequant.data_ptr(), _OUT_FORMATS[out_format])
+            None if out_dequant is None else out_dequant.data_ptr(), _OUT_FORMATS[out_format],
+            None if row_sumsq is None else row_sumsq.data_ptr())
     cw0 = w0.c()
     cw1 = w1.c() if w1 is not None else None
     epi = MOE_EPI_SWIGLU if w1 is not None else MOE_EPI_NONE
@@ -288,7 +324,29 @@ def tile_weights(w: Weights, stream=None) -> Weights:
     scale = torch.empty_like(w.scale)
     _check(lib.moe_fp4_tile_weights(w.format, E, n, 2 * k2, _ptr(w.packed), _ptr(w.scale), _ptr(packed), _ptr(scale),
                                     _stream(stream)), "moe_fp4_tile_weights")
-    return Weights(packed, scale, w.global_scale, w.scales_pow2, tiled=True, mx_exact=w.mx_exact)
+    return Weights(packed, scale, w.global_scale, w.scales_pow2, tiled=True, mx_exact=w.mx_exact, compact=w.compact)
+
+
+def compact_mx(mx_scale: torch.Tensor, packed: torch.Tensor, codes=None, base=None, cnt=None, stream=None):
+    """mx_scale u8 [M, n, k/32], packed u8 [M, n, k/2] -> (exponent codes u8 [M, n, k/64],
+    base f32 [M], counters i64 [4]: blocks, all-zero below the window, re-rounded, NaN)."""
+    M, n, kb = mx_scale.shape
+    k = kb * 32
+    dev = mx_scale.device
+    codes = torch.empty((M, n, k // 64), dtype=torch.uint8, device=dev) if codes is None else codes
+    base = torch.empty(M, dtype=torch.float32, device=dev) if base is None else base
+    cnt = torch.empty(4, dtype=torch.int64, device=dev) if cnt is None else cnt
+    _check(lib.moe_fp4_compact_mx(_ptr(mx_scale), _ptr(packed), M, n, k, _ptr(codes), _ptr(base), _ptr(cnt),
+                                  _stream(stream)), "moe_fp4_compact_mx")
+    return codes, base, cnt
+
+
+def compact_weights(w: Weights, stream=None):
+    """Compact copy of row-major MXFP4 weights (codes shared) -> (Weights, counters i64 [4])."""
+    if w.format != MOE_FP4_MX or w.tiled:
+        raise ValueError("compact_weights takes row-major MXFP4 weights")
+    codes, base, cnt = compact_mx(w.scale, w.packed, stream=stream)
+    return Weights(w.packed, codes, base, compact=True), cnt
 
 
 def quantize_nvfp4(x: torch.Tensor, input_scale: float = 1.0, codes=None, scales=None, dequant=None, stream=None):
@@ -300,6 +358,17 @@ def quantize_nvfp4(x: torch.Tensor, input_scale: float = 1.0, codes=None, scales
     _check(lib.moe_quantize_nvfp4(_ptr(x), rows, k, float(input_scale), _ptr(codes), _ptr(scales), _ptr(dequant),
                                   _stream(stream)), "moe_quantize_nvfp4")
     return codes, scales
+
+
+def reap_saliency_accumulate(row_sumsq: torch.Tensor, offsets: torch.Tensor, sorted_slots: torch.Tensor,
+                             topk_weights: torch.Tensor, sums: torch.Tensor, counts: torch.Tensor, rows: int,
+                             stream=None):
+    """sums (float64 [E]) += per-expert sum of g * ||o_row||; counts (int64 [E]) += rows per expert."""
+    E = sums.numel()
+    _check(lib.moe_reap_saliency_accumulate(_ptr(row_sumsq), rows, row_sumsq.shape[1], _ptr(offsets), E,
+                                            _ptr(sorted_slots), _ptr(topk_weights), _ptr(sums), _ptr(counts),
+                                            _stream(stream)), "moe_reap_saliency_accumulate")
+    return sums, counts
 
 
 def quantize_mxfp8(x: torch.Tensor, codes=None, scales=None, stream=None):

@@ -29,17 +29,23 @@ moe_status launch_route(const float*, const float*, int64_t, const moe_route_par
 size_t permute_ws_bytes(int64_t R, int E);
 moe_status launch_permute(const int32_t*, int64_t, int, int, int32_t*, int32_t*, int32_t*, void*, hipStream_t);
 bool route_permute_fits(int64_t T, int top_k);
+size_t route_gemv_ws_bytes(int64_t T, int E);
+moe_status launch_route_gemv(const void*, const float*, const float*, int64_t, int, const moe_route_params*, int32_t*,
+                             float*, void*, hipStream_t);
 moe_status launch_route_permute(const float*, const float*, int64_t, const moe_route_params*, int32_t*, float*, int32_t*,
                                 int32_t*, int32_t*, uint32_t*, hipStream_t);
 moe_status launch_combine(const void*, const int32_t*, const float*, const void*, int64_t, int, int, void*, hipStream_t);
 moe_status launch_transcode(const uint8_t*, const uint8_t*, int64_t, int, int, uint8_t*, float*, int64_t*, hipStream_t);
 moe_status launch_quant(const void*, int64_t, int, float, uint8_t*, uint8_t*, void*, hipStream_t);
-moe_status launch_tile(bool, int64_t, int, int, const uint8_t*, const uint8_t*, uint8_t*, uint8_t*, hipStream_t);
+moe_status launch_tile(int, int64_t, int, int, const uint8_t*, const uint8_t*, uint8_t*, uint8_t*, hipStream_t);
 moe_status launch_gemm_decode(const GemmArgs&, bool swiglu, int wf, bool a_nv, int64_t rows, hipStream_t);
 moe_status launch_gemm_prefill(const GemmArgs&, bool swiglu, int wf, bool a_nv, int64_t rows, hipStream_t);
 moe_status launch_gemm_scaled(const GemmArgs&, bool swiglu, bool planes, bool w_nv, hipStream_t);
 moe_status launch_quant_mxfp8(const void*, int64_t, int, uint8_t*, uint8_t*, hipStream_t);
+moe_status launch_saliency(const float*, int64_t, int, const int32_t*, int, const int32_t*, const float*, double*,
+                           int64_t*, hipStream_t);
 moe_status launch_quant_planes(const void*, int64_t, int, float, uint8_t*, uint8_t*, hipStream_t);
+moe_status launch_compact(const uint8_t*, const uint8_t*, int64_t, int, int, uint8_t*, float*, int64_t*, hipStream_t);
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -157,19 +163,49 @@ moe_status moe_route_permute(const float* logits, const float* correction_bias, 
                               slot_rows, counter, stream);
 }
 
+size_t moe_route_gemv_workspace_bytes(int64_t T, int32_t num_experts) {
+  if (T < 0 || num_experts <= 0) return 0;
+  return route_gemv_ws_bytes(T, num_experts);
+}
+
+moe_status moe_route_gemv(const void* x, const float* gate_weight, const float* correction_bias, int64_t T,
+                          int32_t hidden, const moe_route_params* p, int32_t* topk_ids, float* topk_weights,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  const moe_status st = check_route(p, T);
+  if (st != MOE_OK) return st;
+  MOE_CHECK(hidden >= 512 && hidden % 512 == 0, "moe_route_gemv: hidden %d must be a positive multiple of 512", hidden);
+  MOE_CHECK(T <= (int64_t)65535 * 16, "moe_route_gemv: T > 1048560");
+  if (T == 0) return MOE_OK;
+  MOE_CHECK(x && gate_weight && topk_ids && topk_weights, "moe_route_gemv: NULL pointer");
+  MOE_CHECK(aligned16(x) && aligned16(gate_weight), "moe_route_gemv: x and gate_weight must be 16-byte aligned");
+  const size_t need = route_gemv_ws_bytes(T, p->num_experts);
+  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) {
+    set_error("moe_route_gemv: workspace %zu bytes < %zu (or NULL / unaligned)", workspace_bytes, need);
+    return MOE_ERR_WORKSPACE;
+  }
+  return launch_route_gemv(x, gate_weight, correction_bias, T, hidden, p, topk_ids, topk_weights, workspace, stream);
+}
+
 static moe_status check_weights(const moe_fp4_weights* w, const char* name) {
   MOE_CHECK(w != nullptr, "moe_fp4_grouped_gemm: %s is NULL", name);
-  MOE_CHECK(w->format == MOE_FP4_MX || w->format == MOE_FP4_NV, "moe_fp4_grouped_gemm: %s bad format", name);
+  MOE_CHECK(w->format == MOE_FP4_MX || w->format == MOE_FP4_NV || w->format == MOE_FP4_MXC,
+            "moe_fp4_grouped_gemm: %s bad format", name);
   MOE_CHECK(w->num_experts >= 1 && w->n >= 16 && w->k >= 128, "moe_fp4_grouped_gemm: %s bad shape", name);
   MOE_CHECK(w->packed && w->scale, "moe_fp4_grouped_gemm: %s NULL data", name);
   MOE_CHECK(aligned16(w->packed), "moe_fp4_grouped_gemm: %s codes not 16-byte aligned", name);
-  if (w->format == MOE_FP4_NV) MOE_CHECK(w->global_scale != nullptr, "moe_fp4_grouped_gemm: %s NV without global", name);
+  if (w->format != MOE_FP4_MX)
+    MOE_CHECK(w->global_scale != nullptr, "moe_fp4_grouped_gemm: %s NV / MXC without global scales", name);
   MOE_CHECK((w->flags & ~(MOE_FP4_SCALES_POW2 | MOE_FP4_TILED | MOE_FP4_MX_EXACT)) == 0,
             "moe_fp4_grouped_gemm: %s unknown flags 0x%x", name, w->flags);
   MOE_CHECK(w->format == MOE_FP4_NV || (w->flags & (MOE_FP4_SCALES_POW2 | MOE_FP4_MX_EXACT)) == 0,
             "moe_fp4_grouped_gemm: %s scale flags are for NV weights", name);
   if (w->k % 128 != 0 || w->n % 16 != 0) {
     set_error("moe_fp4_grouped_gemm: %s needs k %% 128 == 0 and n %% 16 == 0 (n=%d k=%d)", name, w->n, w->k);
+    return MOE_ERR_UNSUPPORTED;
+  }
+  if (w->format == MOE_FP4_MXC && w->k % 512 != 0) {
+    set_error("moe_fp4_grouped_gemm: %s compact weights need k %% 512 == 0 (k=%d)", name, w->k);
     return MOE_ERR_UNSUPPORTED;
   }
   if (w->flags & MOE_FP4_TILED) {
@@ -234,6 +270,24 @@ moe_status moe_fp4_grouped_gemm(const moe_act* a, const moe_fp4_weights* w0, con
     }
   }
   MOE_CHECK(algo >= MOE_ALGO_AUTO && algo <= MOE_ALGO_PREFILL, "moe_fp4_grouped_gemm: bad algo");
+  if (out->row_sumsq) {
+    MOE_CHECK(epi == MOE_EPI_NONE, "moe_fp4_grouped_gemm: row_sumsq is for the down projection (MOE_EPI_NONE)");
+    MOE_CHECK(((uintptr_t)out->row_sumsq & 3) == 0, "moe_fp4_grouped_gemm: row_sumsq not 4-byte aligned");
+    // the sums come from the MFMA-tiled kernels' epilogue
+    if (algo == MOE_ALGO_DECODE || w0->n % 256 != 0 || w0->k % 256 != 0 || w0->num_experts > 1000) {
+      set_error("moe_fp4_grouped_gemm: row_sumsq needs the MFMA-tiled kernels (algo AUTO or PREFILL, n %% 256 == 0, "
+                "k %% 256 == 0, <= 1000 experts)");
+      return MOE_ERR_UNSUPPORTED;
+    }
+  }
+  if (w0->format == MOE_FP4_MXC) {
+    // the compact format is the weight-streaming kernel's (decode) storage
+    if (scaled || out->row_sumsq || algo == MOE_ALGO_PREFILL) {
+      set_error("moe_fp4_grouped_gemm: compact (MXC) weights run the weight-streaming kernel only: BF16 / NVFP4 "
+                "activations, algo AUTO or DECODE, no row_sumsq");
+      return MOE_ERR_UNSUPPORTED;
+    }
+  }
   if (scaled) {
     MOE_CHECK(w0->format == MOE_FP4_MX || (w0->flags & MOE_FP4_MX_EXACT),
               "moe_fp4_grouped_gemm: block-scaled MFMA modes need MX weights or NV weights flagged MX_EXACT");
@@ -274,6 +328,7 @@ moe_status moe_fp4_grouped_gemm(const moe_act* a, const moe_fp4_weights* w0, con
   g.out_dq = (uint16_t*)out->dequant;
   g.out_g = nvfp4_out ? out->output_scale : 1.0f;
   g.out_format = out->format;
+  g.out_sumsq = out->row_sumsq;
   {
     int e;
     (void)frexpf(g.out_g, &e);
@@ -283,11 +338,14 @@ moe_status moe_fp4_grouped_gemm(const moe_act* a, const moe_fp4_weights* w0, con
 
   const bool swiglu = epi == MOE_EPI_SWIGLU;
   if (scaled) return launch_gemm_scaled(g, swiglu, a->mode == MOE_ACT_NVFP4_PLANES, w0->format == MOE_FP4_NV, stream);
-  // weight scale format: 0 MXFP4, 1 NVFP4 with power-of-two scales, 2 NVFP4 with any scales
-  const int wf = w0->format == MOE_FP4_MX ? 0 : ((w0->flags & (MOE_FP4_SCALES_POW2 | MOE_FP4_MX_EXACT)) ? 1 : 2);
+  // weight scale format: 0 MXFP4, 1 NVFP4 with power-of-two scales, 2 NVFP4 with any scales, 3 compact MXFP4
+  const int wf = w0->format == MOE_FP4_MX    ? 0
+                 : w0->format == MOE_FP4_MXC ? 3
+                                             : ((w0->flags & (MOE_FP4_SCALES_POW2 | MOE_FP4_MX_EXACT)) ? 1 : 2);
   const bool a_nv = a->mode == MOE_ACT_NVFP4;
+  if (wf == 3) return launch_gemm_decode(g, swiglu, wf, a_nv, rows, stream);
   int use = algo;
-  if (use == MOE_ALGO_AUTO) use = (rows >= 32LL * g.E) ? MOE_ALGO_PREFILL : MOE_ALGO_DECODE;
+  if (use == MOE_ALGO_AUTO) use = (rows >= 32LL * g.E || out->row_sumsq) ? MOE_ALGO_PREFILL : MOE_ALGO_DECODE;
   if (use == MOE_ALGO_PREFILL) return launch_gemm_prefill(g, swiglu, wf, a_nv, rows, stream);
   return launch_gemm_decode(g, swiglu, wf, a_nv, rows, stream);
 }
@@ -319,11 +377,27 @@ moe_status fp4_transcode_mx_to_nv(const uint8_t* mx_scale, const uint8_t* packed
   return launch_transcode(mx_scale, packed, num_mats, n, k, nv_scale, global_scale, counters, stream);
 }
 
+moe_status moe_fp4_compact_mx(const uint8_t* mx_scale, const uint8_t* packed, int64_t num_mats, int32_t n, int32_t k,
+                              uint8_t* exp_codes, float* global_base, int64_t* counters, hipStream_t stream) {
+  g_err[0] = 0;
+  MOE_CHECK(num_mats >= 0 && n >= 16 && k >= 512, "moe_fp4_compact_mx: bad sizes");
+  MOE_CHECK(k % 512 == 0 && n % 16 == 0, "moe_fp4_compact_mx: needs k %% 512 == 0 and n %% 16 == 0");
+  MOE_CHECK(counters != nullptr && ((uintptr_t)counters & 7) == 0, "moe_fp4_compact_mx: counters NULL or unaligned");
+  MOE_CHECK(num_mats * (int64_t)n * (k / 32) < ((int64_t)1 << 40), "moe_fp4_compact_mx: too many blocks");
+  if (num_mats > 0) {
+    MOE_CHECK(mx_scale && packed && exp_codes && global_base, "moe_fp4_compact_mx: NULL pointer");
+    MOE_CHECK(aligned16(mx_scale) && aligned16(packed) && aligned16(exp_codes),
+              "moe_fp4_compact_mx: buffers must be 16-byte aligned");
+    MOE_CHECK(num_mats < ((int64_t)1 << 31), "moe_fp4_compact_mx: too many matrices");
+  }
+  return launch_compact(mx_scale, packed, num_mats, n, k, exp_codes, global_base, counters, stream);
+}
+
 moe_status moe_fp4_tile_weights(moe_fp4_format format, int32_t num_experts, int32_t n, int32_t k,
                                 const uint8_t* packed, const uint8_t* scale, uint8_t* packed_tiled,
                                 uint8_t* scale_tiled, hipStream_t stream) {
   g_err[0] = 0;
-  MOE_CHECK(format == MOE_FP4_MX || format == MOE_FP4_NV, "moe_fp4_tile_weights: bad format");
+  MOE_CHECK(format == MOE_FP4_MX || format == MOE_FP4_NV || format == MOE_FP4_MXC, "moe_fp4_tile_weights: bad format");
   MOE_CHECK(num_experts >= 0 && n >= 16 && k >= 512, "moe_fp4_tile_weights: bad sizes");
   MOE_CHECK(n % 16 == 0 && k % 512 == 0, "moe_fp4_tile_weights: needs n %% 16 == 0 and k %% 512 == 0");
   if (num_experts == 0) return MOE_OK;
@@ -331,7 +405,8 @@ moe_status moe_fp4_tile_weights(moe_fp4_format format, int32_t num_experts, int3
   MOE_CHECK(aligned16(packed) && aligned16(scale) && aligned16(packed_tiled) && aligned16(scale_tiled),
             "moe_fp4_tile_weights: buffers must be 16-byte aligned");
   const uint64_t cb = (uint64_t)num_experts * (uint64_t)n * (uint64_t)(k / 2);
-  const uint64_t sb = (uint64_t)num_experts * (uint64_t)n * (uint64_t)(format == MOE_FP4_NV ? k / 16 : k / 32);
+  const uint64_t sb = (uint64_t)num_experts * (uint64_t)n *
+                      (uint64_t)(format == MOE_FP4_NV ? k / 16 : format == MOE_FP4_MXC ? k / 64 : k / 32);
   auto overlap = [](const void* a, uint64_t na, const void* b, uint64_t nb) {
     const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
     return x < y + nb && y < x + na;
@@ -340,7 +415,8 @@ moe_status moe_fp4_tile_weights(moe_fp4_format format, int32_t num_experts, int3
                 !overlap(packed, cb, scale_tiled, sb) && !overlap(scale, sb, packed_tiled, cb) &&
                 !overlap(packed_tiled, cb, scale_tiled, sb),
             "moe_fp4_tile_weights: outputs overlap inputs or each other");
-  return launch_tile(format == MOE_FP4_NV, num_experts, n, k, packed, scale, packed_tiled, scale_tiled, stream);
+  return launch_tile(format == MOE_FP4_NV ? 1 : (format == MOE_FP4_MXC ? 2 : 0), num_experts, n, k, packed, scale,
+                     packed_tiled, scale_tiled, stream);
 }
 
 moe_status moe_quantize_nvfp4(const void* x, int64_t rows, int32_t k, float input_scale, uint8_t* codes,
@@ -353,6 +429,21 @@ moe_status moe_quantize_nvfp4(const void* x, int64_t rows, int32_t k, float inpu
   MOE_CHECK(aligned16(x) && ((uintptr_t)codes & 7u) == 0, "moe_quantize_nvfp4: misaligned buffers");
   if (dequant) MOE_CHECK(aligned16(dequant), "moe_quantize_nvfp4: dequant output not 16-byte aligned");
   return launch_quant(x, rows, k, input_scale, codes, scales, dequant, stream);
+}
+
+moe_status moe_reap_saliency_accumulate(const float* row_sumsq, int64_t rows, int32_t parts,
+                                        const int32_t* expert_offsets, int32_t num_experts,
+                                        const int32_t* sorted_slots, const float* topk_weights, double* saliency_sum,
+                                        int64_t* counts, hipStream_t stream) {
+  g_err[0] = 0;
+  MOE_CHECK(rows >= 0 && parts >= 1 && num_experts >= 0, "moe_reap_saliency_accumulate: bad sizes");
+  if (rows == 0 || num_experts == 0) return MOE_OK;
+  MOE_CHECK(row_sumsq && expert_offsets && sorted_slots && topk_weights && saliency_sum && counts,
+            "moe_reap_saliency_accumulate: NULL pointer");
+  MOE_CHECK(((uintptr_t)saliency_sum & 7) == 0 && ((uintptr_t)counts & 7) == 0,
+            "moe_reap_saliency_accumulate: sums / counts not 8-byte aligned");
+  return launch_saliency(row_sumsq, rows, parts, expert_offsets, num_experts, sorted_slots, topk_weights, saliency_sum,
+                         counts, stream);
 }
 
 moe_status moe_quantize_mxfp8(const void* x, int64_t rows, int32_t k, uint8_t* codes, uint8_t* scales,

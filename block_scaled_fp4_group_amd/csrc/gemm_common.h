@@ -28,6 +28,7 @@ struct GemmArgs {
   float out_g;                    // output global scale
   int out_format;                 // MOE_OUT_NVFP4 / MOE_OUT_MXFP8 / MOE_OUT_NVFP4_PLANES (codes, scales)
   int out_g_log2;                 // log2(out_g) (NVFP4 planes: folded into their E8M0 scales)
+  float* out_sumsq;               // [rows, N/64]: per-row sums of squares of the FP32 outputs, or null
   int tiled;                      // weights in the tiled layout (host-side dispatch)
 };
 
@@ -35,18 +36,21 @@ struct GemmArgs {
 // holds row li, code chunk lg of each 128-column step and row li's scales of
 // each 4-step window; the tile's own base and the step / window count are
 // added by the caller (a tile spans 16 * K/2 code bytes and 16 * sc_row scale
-// bytes in either layout).
-template <bool TL, bool W_NV>
-struct WeightLane {
+// bytes in either layout).  WB: scale bytes per row and 4-step (512-column)
+// window -- MXFP4 16 (E8M0), NVFP4 32 (E4M3), compact MXFP4 8 (4-bit codes).
+template <bool TL, int WB>
+struct WeightLaneB {
   static constexpr uint32_t kStep = TL ? 1024u : 64u;                       // code bytes per step
-  static constexpr uint32_t kWin = TL ? (W_NV ? 512u : 256u) : (W_NV ? 32u : 16u);   // scale bytes per window
+  static constexpr uint32_t kWin = TL ? 16u * WB : (uint32_t)WB;             // scale bytes per window
   __host__ __device__ static uint32_t code(int li, int lg, int K) {
     return TL ? (uint32_t)(lg * 16 + li) * 16u : (uint32_t)li * (uint32_t)(K / 2) + (uint32_t)lg * 16u;
   }
   __host__ __device__ static uint32_t scale(int li, int K) {
-    return TL ? (uint32_t)li * (W_NV ? 32u : 16u) : (uint32_t)li * (uint32_t)(W_NV ? K / 16 : K / 32);
+    return TL ? (uint32_t)li * (uint32_t)WB : (uint32_t)li * (uint32_t)(K / (512 / WB));
   }
 };
+template <bool TL, bool W_NV>
+using WeightLane = WeightLaneB<TL, W_NV ? 32 : 16>;
 
 // Locate the j-th expert with at least one row (experts in index order).
 // Returns false when fewer than j+1 experts are active.  All threads of the

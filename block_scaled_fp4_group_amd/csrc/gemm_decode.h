@@ -64,15 +64,20 @@ __device__ __forceinline__ uint32_t quant4_across_lanes(const float* v, float in
 }
 
 // WF: weight scale format -- 0 MXFP4 (E8M0 per 32), 1 NVFP4 whose E4M3 scales
-// are all powers of two (the exact MXFP4 transcode), 2 NVFP4 with any scales.
+// are all powers of two (the exact MXFP4 transcode), 2 NVFP4 with any scales,
+// 3 compact MXFP4 (4-bit exponent code c per 32: scale 2^c here, the matrix's
+// base 2^b applied with the global scales in the epilogue -- a power-of-two
+// factor on every product, so the sums are those of the MXFP4 path times 2^-b).
 template <int NMAT, int WF, bool TL = false>
 struct DecodeWave {
-  static constexpr bool W_NV = WF != 0;
-  using WL = WeightLane<TL, W_NV>;
+  static constexpr bool W_NV = WF == 1 || WF == 2;
+  static constexpr bool W_CP = WF == 3;
+  static constexpr int WB = W_CP ? 8 : (W_NV ? 32 : 16);
+  using WL = WeightLaneB<TL, WB>;
   static constexpr bool W_GEN = WF == 2;     // general E4M3 scales: convert through float
-  static constexpr int SWN = W_NV ? 2 : 1;   // dwordx4 per scale window
+  static constexpr int SWN = W_NV ? 2 : 1;   // dwordx4 per scale window (compact: its low half)
   rsrc_t wr_[NMAT];          // this expert's codes [N, K/2]
-  rsrc_t sr_[NMAT];          // this expert's scales [N, K/32] | [N, K/16]
+  rsrc_t sr_[NMAT];          // this expert's scales [N, K/32] | [N, K/16] | [N, K/64]
   uint32_t wo;               // code offset of (row n0+li, block 4*st0+lg), first tile
   uint32_t so;               // scale offset of (row n0+li, block 4*st0), first tile
   uint32_t wtile, stile;     // offset from one 16-row tile to the next (codes, scales)
@@ -89,15 +94,22 @@ struct DecodeWave {
 #pragma unroll
     for (int s = 0; s < 4; ++s) S.a[s] = a4[s];
   }
-  // scale window of super-step c of tile t (4 steps x 4 lane groups): MX 16 B, NV 32 B
+  // scale window of super-step c of tile t (4 steps x 4 lane groups): MX 16 B, NV 32 B, compact 8 B
   __device__ __forceinline__ void sload(u32x4 (&W)[NMAT][SWN], int t, int c) const {
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m)
+    for (int m = 0; m < NMAT; ++m) {
+      if (W_CP) {
+        const u32x2 v = bload64(sr_[m], so + t * stile + c * WL::kWin, 0);
+        W[m][0] = u32x4{v[0], v[1], 0u, 0u};
+      } else {
 #pragma unroll
-      for (int h = 0; h < SWN; ++h) W[m][h] = bload128(sr_[m], so + t * stile + c * WL::kWin + 16 * h, 0);
+        for (int h = 0; h < SWN; ++h) W[m][h] = bload128(sr_[m], so + t * stile + c * WL::kWin + 16 * h, 0);
+      }
+    }
   }
-  // this lane's scale bits (E8M0 byte, or two E4M3 bytes) for step j of a window
+  // this lane's scale bits (E8M0 byte, two E4M3 bytes, or a 4-bit code) for step j of a window
   __device__ __forceinline__ uint32_t sbits(const u32x4 (&W)[SWN], int j) const {
+    if (W_CP) return (W[0][j >> 1] >> (4 * (4 * (j & 1) + lg))) & 0xFu;   // block 4j + lg: nibble of dword j/2
     if (W_NV) {                 // dword 2j + lg / 2 of the window, chosen by a select (no indexed registers)
       const uint32_t d0 = W[(2 * j) >> 2][(2 * j) & 3], d1 = W[(2 * j + 1) >> 2][(2 * j + 1) & 3];
       return (((lg >> 1) ? d1 : d0) >> (16 * (lg & 1))) & 0xFFFFu;
@@ -107,6 +119,7 @@ struct DecodeWave {
   // this lane's scale bits for own step i of tile t, loaded on their own (remainder steps)
   __device__ __forceinline__ uint32_t sbits_direct(int m, int t, int i) const {
     if (W_NV) return bload16(sr_[m], so + t * stile + (4 * i + lg) * 2, 0);
+    if (W_CP) return (bload8(sr_[m], so + t * stile + ((4 * i + lg) >> 1), 0) >> (4 * (lg & 1))) & 0xFu;
     return bload8(sr_[m], so + t * stile + 4 * i + lg, 0);
   }
   __device__ __forceinline__ void consume(const WStage<NMAT>& W, const AStage& A, const uint32_t (&sb)[NMAT]) {
@@ -119,6 +132,8 @@ struct DecodeWave {
       if (W_NV) {
         s_lo = e4m3_byte<0>(sb[m]);
         s_hi = e4m3_byte<1>(sb[m]);
+      } else if (W_CP) {
+        s_lo = s_hi = __uint_as_float((sb[m] + 127u) << 23);   // 2^c, c in [0, 15]
       } else {
         s_lo = s_hi = e8m0_to_f32(sb[m]);
       }
@@ -294,7 +309,6 @@ __host__ __device__ constexpr int decode_pitch(int K) { return K * 2 + 16; }
 
 template <int NMAT, int NWN, int KS, int NT, int NS, int WF, bool A_NV, bool TL>
 __global__ __launch_bounds__(NWN * KS * 64) void gemm_decode_kernel(GemmArgs p) {
-  constexpr bool W_NV = WF != 0;
   // the general NVFP4 conversion needs more registers: a shorter weight ring
   constexpr int PF = NMAT == 2 ? (WF == 2 ? 4 : kDecRing2) : kDecRing1, PA = 2;
   static_assert(KS == 1 || NT == 1, "the K split runs one tile per wave");
@@ -318,11 +332,12 @@ __global__ __launch_bounds__(NWN * KS * 64) void gemm_decode_kernel(GemmArgs p) 
   const int ns = NS > 0 ? NS : (K / 128) / KS;                // own steps per tile (contiguous range)
   const int st0 = ks * ns;                                    // first global step
 
-  DecodeWave<NMAT, WF, TL> dw;
-  using WL = WeightLane<TL, W_NV>;
+  using DW = DecodeWave<NMAT, WF, TL>;
+  DW dw;
+  using WL = typename DW::WL;
   dw.lg = lg;
   const uint32_t mat_codes = (uint32_t)N * (uint32_t)(K / 2);
-  const uint32_t sc_row = (uint32_t)(W_NV ? K / 16 : K / 32);
+  const uint32_t sc_row = (uint32_t)(K / (512 / DW::WB));
   const uint32_t mat_scales = (uint32_t)N * sc_row;
 #pragma unroll
   for (int m = 0; m < NMAT; ++m) {
@@ -337,7 +352,7 @@ __global__ __launch_bounds__(NWN * KS * 64) void gemm_decode_kernel(GemmArgs p) 
 
   float wglob[NMAT];
 #pragma unroll
-  for (int m = 0; m < NMAT; ++m) wglob[m] = W_NV ? p.w_global[m][e] : 1.0f;
+  for (int m = 0; m < NMAT; ++m) wglob[m] = WF != 0 ? p.w_global[m][e] : 1.0f;   // NV global | compact base
 
   __shared__ f32x4 red[KS > 1 ? (KS - 1) * NWN * NMAT * 64 : 1];
 
@@ -404,8 +419,10 @@ static void launch_decode_t(const GemmArgs& a, int wf, bool a_nv, int nact, hipS
                  : launch_decode_one<NMAT, NWN, KS, NT, NS, 0, false, TL>(a, nact, stream); break;
     case 1: a_nv ? launch_decode_one<NMAT, NWN, KS, NT, NS, 1, true, TL>(a, nact, stream)
                  : launch_decode_one<NMAT, NWN, KS, NT, NS, 1, false, TL>(a, nact, stream); break;
-    default: a_nv ? launch_decode_one<NMAT, NWN, KS, NT, NS, 2, true, TL>(a, nact, stream)
-                  : launch_decode_one<NMAT, NWN, KS, NT, NS, 2, false, TL>(a, nact, stream); break;
+    case 2: a_nv ? launch_decode_one<NMAT, NWN, KS, NT, NS, 2, true, TL>(a, nact, stream)
+                 : launch_decode_one<NMAT, NWN, KS, NT, NS, 2, false, TL>(a, nact, stream); break;
+    default: a_nv ? launch_decode_one<NMAT, NWN, KS, NT, NS, 3, true, TL>(a, nact, stream)
+                  : launch_decode_one<NMAT, NWN, KS, NT, NS, 3, false, TL>(a, nact, stream); break;
   }
 }
 

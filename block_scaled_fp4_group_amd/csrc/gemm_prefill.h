@@ -273,6 +273,9 @@ __device__ __forceinline__ void pf_compute(const uint8_t* st, const uint8_t* ss,
 }
 
 // Epilogue: lane holds D[weight row 4*lg + i of group g][token row li of group t].
+// (One matrix: with p.out_sumsq, the sum of squares of the row's FP32 outputs
+// over the wave's 64 columns goes to out_sumsq[row, column / 64] -- the REAP
+// saliency's per-row norm, in parts that a later pass adds in order.)
 template <int NMAT>
 __device__ __forceinline__ void pf_epilogue(const GemmArgs& p, const PfTile& T, const f32x4 (&acc)[4][4],
                                             const float (&wglob)[NMAT], int wm, int wn, int li, int lg) {
@@ -282,6 +285,7 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& p, const PfTile& T, 
     const int mrow = wm * 64 + t * 16 + li;
     const bool ok = mrow < T.mrows;
     const int64_t ro = T.rbase + mrow;
+    float sq = 0.0f;
 #pragma unroll
     for (int gp = 0; gp < (NMAT == 2 ? 2 : 4); ++gp) {
       float v[4];
@@ -289,6 +293,7 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& p, const PfTile& T, 
       for (int i = 0; i < 4; ++i) {
         const float g = acc[gp][t][i] * wglob[0];
         v[i] = NMAT == 2 ? silu_f(g) * (acc[gp + 2][t][i] * wglob[NMAT - 1]) : g;
+        if (NMAT == 1) sq = fmaf(v[i], v[i], sq);
       }
       const int col = T.nbase + (NMAT == 2 ? wn * 32 + gp * 16 : wn * 64 + gp * 16) + 4 * lg;
       const uint32_t b01 = pack_bf16x2(v[0], v[1]), b23 = pack_bf16x2(v[2], v[3]);
@@ -305,6 +310,12 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& p, const PfTile& T, 
           if (p.out_dq) *(u32x2*)(p.out_dq + ro * N + col) = nvfp4_dequant4(bits, e4m3_to_f32(sb) * p.out_g);
         }
       }
+    }
+    if (NMAT == 1 && p.out_sumsq) {
+      // lanes li + 16 lg hold the 4 x 4 columns of each group: add the four lane groups in a fixed order
+      const float s1 = sq + __shfl_xor(sq, 16, kWave);
+      const float s2 = s1 + __shfl_xor(s1, 32, kWave);
+      if (ok && lg == 0) p.out_sumsq[ro * (N / 64) + (T.nbase + wn * 64) / 64] = s2;
     }
   }
 }

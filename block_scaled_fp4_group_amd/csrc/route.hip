@@ -114,22 +114,27 @@ __device__ __forceinline__ void top2_segment(double& b1, double& b2, int levels)
 // block must call it (it synchronises the block).
 static_assert(kPermThreads == 256, "the router block runs the permutation");
 
-__device__ __forceinline__ void route_tokens(const float* __restrict__ logits, const float* __restrict__ bias,
-                                             int64_t T, int E, int n_group, int topk_group, int top_k, float scale,
-                                             int norm, int32_t* __restrict__ ids, float* __restrict__ weights) {
-  __shared__ double gscore[kRouteWaves][64];
-  __shared__ double cval[kRouteWaves][256];
+// Wave wv routes token tb + wv; the logits are FP32 (the router output as
+// stored) or float64 (the fused router matmul's own sums).
+template <typename LT, int NW = kRouteWaves>
+__device__ __forceinline__ void route_tokens(const LT* __restrict__ logits, const float* __restrict__ bias,
+                                             int64_t tb, int64_t T, int E, int n_group, int topk_group, int top_k,
+                                             float scale, int norm, int32_t* __restrict__ ids,
+                                             float* __restrict__ weights) {
+  __shared__ double gscore[NW][64];
+  __shared__ double cval[NW][256];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
-  const int64_t t0 = (int64_t)blockIdx.x * kRouteWaves + wv;
+  const int64_t t0 = tb + wv;
   const bool valid = t0 < T;           // no early exit: the block synchronises below
   const int64_t t = valid ? t0 : T - 1;
   const int gs = E / n_group;
   const bool pow2 = (gs & (gs - 1)) == 0;
-  const float* lrow = logits + t * E;
+  const LT* lrow = logits + t * E;
 
   // every load in flight at once (lanes past E read expert E - 1 and drop it)
-  float lv[kRouteMaxPer], bv[kRouteMaxPer];
+  LT lv[kRouteMaxPer];
+  float bv[kRouteMaxPer];
 #pragma unroll
   for (int j = 0; j < kRouteMaxPer; ++j) lv[j] = lrow[min(lane + 64 * j, E - 1)];
   if (bias) {
@@ -253,7 +258,8 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
                                                     int n_group, int topk_group, int top_k, float scale,
                                                     int norm, int32_t* __restrict__ ids,
                                                     float* __restrict__ weights) {
-  route_tokens(logits, bias, T, E, n_group, topk_group, top_k, scale, norm, ids, weights);
+  route_tokens(logits, bias, (int64_t)blockIdx.x * kRouteWaves, T, E, n_group, topk_group, top_k, scale, norm, ids,
+               weights);
 }
 
 // Router and permutation in one launch (R = T * top_k <= kPermChunk).  Each
@@ -274,7 +280,8 @@ __global__ __launch_bounds__(256) void route_permute_kernel(const float* __restr
                                                             int32_t* __restrict__ slot_rows,
                                                             uint32_t* __restrict__ counter) {
   __shared__ int s_last;
-  route_tokens(logits, bias, T, E, n_group, topk_group, top_k, scale, norm, ids, weights);
+  route_tokens(logits, bias, (int64_t)blockIdx.x * kRouteWaves, T, E, n_group, topk_group, top_k, scale, norm, ids,
+               weights);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // each wave, after its own stores
   __syncthreads();
   if (threadIdx.x == 0) s_last = atomicAdd(counter, 1u) == gridDim.x - 1;
@@ -296,6 +303,101 @@ moe_status launch_route(const float* logits, const float* bias, int64_t T, const
 }
 
 bool route_permute_fits(int64_t T, int top_k) { return T >= 1 && T * top_k <= kPermChunk; }
+
+// ------------------------------------------------- router matmul + top-k
+// The router's matmul and the group top-k in one launch ("MiMo-V2.6-Flash-MOPD
+// on one RTX PRO 6000", "What makes it fast": one matmul and a fused top-k
+// per layer; "MiMo-V2.6-Flash-RL Mixed-Quant GGUF", "Quantization targets":
+// routers stay F32).  logits[t, e] = sum_k x[t, k] W[e, k] for bf16 x and the
+// FP32 weight W: each product is exact in float64 and the sum is float64, in a
+// fixed order, so the selection sees the oracle's float64 logits up to the
+// order of one float64 summation.
+//   * workgroup (b, q) of 16 waves: a 16-token x 16-expert tile (tokens 16q..,
+//     experts 16b..); wave w takes the w-th sixteenth of the hidden dimension
+//     and runs float64 16x16x4 MFMAs over it, each lane group g of the wave
+//     supplying a contiguous quarter of that range (the k of one MFMA is one
+//     value from each lane group), so every lane reads contiguous 16-byte
+//     pieces of its token row and expert row;
+//   * the 16 partial tiles meet in LDS and are added in wave order;
+//   * the workgroups of one 16-token block count themselves in counters[q]
+//     after a device-scope release; the last one (every logit of its tokens is
+//     then behind an acquire) routes the 16 tokens, one per wave, and sets the
+//     counter back to zero.
+constexpr int kGemvWaves = 16;
+constexpr int kGemvTile = 16;
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kGemvWaves * 64) void route_gemv_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ W, const float* __restrict__ bias, int64_t T, int H, int E,
+    int n_group, int topk_group, int top_k, float scale, int norm, int32_t* __restrict__ ids,
+    float* __restrict__ weights, double* __restrict__ logits, uint32_t* __restrict__ counters) {
+  __shared__ double part[kGemvWaves][kGemvTile * kGemvTile];
+  __shared__ int s_last;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t t0 = (int64_t)blockIdx.y * kGemvTile;
+  const int e0 = blockIdx.x * kGemvTile;
+  const int64_t t = min(t0 + r, T - 1);                       // rows past the end reread the last one
+  const int e = min(e0 + r, E - 1);
+  const int kg = H / (kGemvWaves * 4);                         // values per lane group (a multiple of 8)
+  const uint16_t* xr = x + t * H + (int64_t)(wv * 4 + g) * kg;
+  const float* wr = W + (int64_t)e * H + (int64_t)(wv * 4 + g) * kg;
+  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+  for (int m = 0; m < kg; m += 8) {
+    const u32x4 xv = *(const u32x4*)(xr + m);
+    const f32x4 w0 = *(const f32x4*)(wr + m);
+    const f32x4 w1 = *(const f32x4*)(wr + m + 4);
+    // D[token][expert] += x[token][k] W[expert][k]: A = token rows, B = expert columns
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_lo(xv[0]), (double)w0[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_hi(xv[0]), (double)w0[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_lo(xv[1]), (double)w0[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_hi(xv[1]), (double)w0[3], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_lo(xv[2]), (double)w1[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_hi(xv[2]), (double)w1[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_lo(xv[3]), (double)w1[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_hi(xv[3]), (double)w1[3], acc, 0, 0, 0);
+  }
+  // the float64 16x16x4 MFMA leaves D[token g + 4 i][expert r] in lane (r, g), element i (measured)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) part[wv][(g + 4 * i) * kGemvTile + r] = acc[i];
+  __syncthreads();
+  if (threadIdx.x < kGemvTile * kGemvTile) {
+    double sum = 0.0;
+#pragma unroll
+    for (int w = 0; w < kGemvWaves; ++w) sum += part[w][threadIdx.x];
+    const int64_t tt = t0 + threadIdx.x / kGemvTile;
+    const int ee = e0 + threadIdx.x % kGemvTile;
+    if (tt < T && ee < E) logits[tt * E + ee] = sum;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // each wave, after its own stores
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicAdd(&counters[blockIdx.y], 1u) == gridDim.x - 1;
+  __syncthreads();
+  if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  route_tokens<double, kGemvWaves>(logits, bias, t0, T, E, n_group, topk_group, top_k, scale, norm, ids, weights);
+  if (threadIdx.x == 0) atomicExch(&counters[blockIdx.y], 0u);
+}
+
+size_t route_gemv_ws_bytes(int64_t T, int E) {
+  const size_t lg = ((size_t)T * (size_t)E * sizeof(double) + 255) & ~(size_t)255;
+  return lg + (size_t)((T + kGemvTile - 1) / kGemvTile) * sizeof(uint32_t);
+}
+
+moe_status launch_route_gemv(const void* x, const float* W, const float* bias, int64_t T, int H,
+                             const moe_route_params* p, int32_t* ids, float* weights, void* ws, hipStream_t stream) {
+  if (T == 0) return MOE_OK;
+  const int E = p->num_experts;
+  double* logits = (double*)ws;
+  uint32_t* counters = (uint32_t*)((uint8_t*)ws + (((size_t)T * (size_t)E * sizeof(double) + 255) & ~(size_t)255));
+  const dim3 grid((uint32_t)((E + kGemvTile - 1) / kGemvTile), (uint32_t)((T + kGemvTile - 1) / kGemvTile));
+  hipLaunchKernelGGL(route_gemv_kernel, grid, dim3(kGemvWaves * 64), 0, stream, (const uint16_t*)x, W, bias, T, H, E, p->n_group,
+                     p->topk_group, p->top_k, p->routed_scaling_factor, p->norm_topk_prob, ids, weights, logits,
+                     counters);
+  return launch_status("moe_route_gemv");
+}
 
 moe_status launch_route_permute(const float* logits, const float* bias, int64_t T, const moe_route_params* p,
                                 int32_t* ids, float* weights, int32_t* offsets, int32_t* sorted_slots,

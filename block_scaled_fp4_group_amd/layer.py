@@ -24,8 +24,9 @@ from typing import Optional
 
 import torch
 
-from . import (MOE_ALGO_AUTO, Weights, combine, grouped_gemm, permute_workspace_bytes, quantize_mxfp8,
-               quantize_nvfp4, quantize_nvfp4_planes, route_permute)
+from . import (MOE_ALGO_AUTO, Weights, combine, grouped_gemm, permute, permute_workspace_bytes, quantize_mxfp8,
+               quantize_nvfp4, quantize_nvfp4_planes, reap_saliency_accumulate, route_gemv, route_gemv_workspace_bytes,
+               route_permute)
 
 
 @dataclasses.dataclass
@@ -38,7 +39,12 @@ class LayerWeights:
 class MoELayer:
     def __init__(self, weights: LayerWeights, num_experts: int, n_group: int, topk_group: int, top_k: int,
                  routed_scaling_factor: float, max_tokens: int, act_mode: str = "bf16", input_scale: float = 1.0,
-                 keep_z_bf16: bool = False, a_mode: str = "dequant", device="cuda"):
+                 keep_z_bf16: bool = False, a_mode: str = "dequant", router_weight: Optional[torch.Tensor] = None,
+                 saliency: bool = False, device="cuda"):
+        """``router_weight``: FP32 [E, hidden]; with it, forward() may be called
+        without logits and runs the router matmul fused with the top-k.
+        ``saliency``: every forward also accumulates the REAP saliency of each
+        expert (sal_sums / sal_counts; S = sal_sums / sal_counts)."""
         self.w = weights
         self.E, self.n_group, self.topk_group, self.top_k = num_experts, n_group, topk_group, top_k
         self.scale = routed_scaling_factor
@@ -58,6 +64,14 @@ class MoELayer:
         self.slot_rows = torch.empty(R, dtype=i32, device=dev)
         self.ws = torch.empty(max(permute_workspace_bytes(T, top_k, E), 16), dtype=torch.uint8, device=dev)
         self.counter = torch.zeros(1, dtype=i32, device=dev)   # router -> permutation hand-off (left zero)
+        self.router_weight = router_weight
+        self.saliency = saliency
+        if saliency:
+            self.row_sumsq = torch.empty((R, H // 64), dtype=torch.float32, device=dev)
+            self.sal_sums = torch.zeros(E, dtype=torch.float64, device=dev)
+            self.sal_counts = torch.zeros(E, dtype=torch.int64, device=dev)
+        if router_weight is not None:                           # fused router: logits + counters (left zero)
+            self.rws = torch.zeros(route_gemv_workspace_bytes(T, E), dtype=torch.uint8, device=dev)
         self.o = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
         self.y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         if act_mode == "mxfp8" or (act_mode == "nvfp4" and a_mode == "planes"):
@@ -81,7 +95,7 @@ class MoELayer:
                 self.x_dq = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
                 self.z_dq = torch.empty((R, I), dtype=torch.bfloat16, device=dev)
 
-    def forward(self, x: torch.Tensor, logits: torch.Tensor, bias: Optional[torch.Tensor] = None,
+    def forward(self, x: torch.Tensor, logits: Optional[torch.Tensor], bias: Optional[torch.Tensor] = None,
                 residual: Optional[torch.Tensor] = None, algo: int = MOE_ALGO_AUTO, y: Optional[torch.Tensor] = None,
                 events: Optional[dict] = None):
         """``events``: optional {step name: (start, end)} torch.cuda.Event pairs recorded
@@ -93,11 +107,19 @@ class MoELayer:
                 events[name][i].record()
         R = T * self.top_k
         ids, topw = self.ids[:T], self.topw[:T]
-        route_permute(logits, bias, self.E, self.n_group, self.topk_group, self.top_k, self.scale, self.counter, True,
-                      ids=ids, weights=topw, workspace=self.ws, offsets=self.offsets,
-                      sorted_slots=self.sorted_slots[:R], slot_rows=self.slot_rows[:R])
+        if logits is None:
+            # router matmul + top-k in one launch, then the permutation
+            route_gemv(x, self.router_weight, bias, self.E, self.n_group, self.topk_group, self.top_k, self.scale,
+                       self.rws, True, ids=ids, weights=topw)
+            permute(ids, self.E, workspace=self.ws, offsets=self.offsets, sorted_slots=self.sorted_slots[:R],
+                    slot_rows=self.slot_rows[:R])
+        else:
+            route_permute(logits, bias, self.E, self.n_group, self.topk_group, self.top_k, self.scale, self.counter,
+                          True, ids=ids, weights=topw, workspace=self.ws, offsets=self.offsets,
+                          sorted_slots=self.sorted_slots[:R], slot_rows=self.slot_rows[:R])
         z = None if self.z is None else self.z[:R]
         o = self.o[:R]
+        sq = self.row_sumsq[:R] if self.saliency else None
         if self.act_mode == "mxfp8" or (self.act_mode == "nvfp4" and self.a_mode == "planes"):
             planes = self.act_mode == "nvfp4"
             if planes:
@@ -113,7 +135,7 @@ class MoELayer:
             mark("gate_up", 1)
             mark("down", 0)
             grouped_gemm(self.z_q[:R], self.w.down, None, self.offsets, R, a_scales=self.z_qs[:R], out=o, algo=algo,
-                         a_mode=am)
+                         a_mode=am, row_sumsq=sq)
             mark("down", 1)
         elif self.act_mode == "nvfp4" and self.a_mode == "dequant":
             xdq = self.x_dq[:T]
@@ -126,7 +148,7 @@ class MoELayer:
                          want_bf16=keep, out_dequant=self.z_dq[:R], algo=algo)
             mark("gate_up", 1)
             mark("down", 0)
-            grouped_gemm(self.z_dq[:R], self.w.down, None, self.offsets, R, out=o, algo=algo)
+            grouped_gemm(self.z_dq[:R], self.w.down, None, self.offsets, R, out=o, algo=algo, row_sumsq=sq)
             mark("down", 1)
         elif self.act_mode == "nvfp4":
             xc, xs = quantize_nvfp4(x, self.input_scale, self.x_codes[:T], self.x_scales[:T])
@@ -138,7 +160,7 @@ class MoELayer:
             mark("gate_up", 1)
             mark("down", 0)
             grouped_gemm(self.z_codes[:R], self.w.down, None, self.offsets, R, a_scales=self.z_scales[:R],
-                         input_scale=self.input_scale, out=o, algo=algo)
+                         input_scale=self.input_scale, out=o, algo=algo, row_sumsq=sq)
             mark("down", 1)
         else:
             mark("gate_up", 0)
@@ -146,8 +168,10 @@ class MoELayer:
                          gather_div=self.top_k, out=z, algo=algo)
             mark("gate_up", 1)
             mark("down", 0)
-            grouped_gemm(z, self.w.down, None, self.offsets, R, out=o, algo=algo)
+            grouped_gemm(z, self.w.down, None, self.offsets, R, out=o, algo=algo, row_sumsq=sq)
             mark("down", 1)
+        if self.saliency:
+            reap_saliency_accumulate(sq, self.offsets, self.sorted_slots[:R], topw, self.sal_sums, self.sal_counts, R)
         y = self.y[:T] if y is None else y
         combine(o, self.slot_rows[:R], topw, residual, y=y)
         return y

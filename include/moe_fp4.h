@@ -121,6 +121,29 @@ moe_status moe_route_permute(const float* logits, const float* correction_bias, 
                              uint32_t* counter, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+/* ------------------------------------------------ router matmul + route
+ * The router's matmul and the group top-k of moe_route in one launch ("MiMo-
+ * V2.6-Flash-MOPD on one RTX PRO 6000", "What makes it fast": one matmul and a
+ * fused top-k per layer; "MiMo-V2.6-Flash-RL Mixed-Quant GGUF", "Quantization
+ * targets": the router weight stays F32).
+ *   logits[t, e] = sum_k x[t, k] * gate_weight[e, k], each product of a bf16
+ *   and an FP32 value exact in float64, summed in float64 (fixed order); the
+ *   selection and weights then follow moe_route on these float64 logits.
+ *   x bf16 [T, hidden]; gate_weight float [E, hidden]; correction_bias float
+ *   [E] or NULL; topk_ids int32 [T, top_k]; topk_weights float [T, top_k].
+ *   hidden % 512 == 0; T <= 1048560;
+ *   x, gate_weight and workspace 16-byte aligned.
+ * workspace: at least moe_route_gemv_workspace_bytes(T, E) bytes of device
+ * memory, ZEROED before its first use; every call leaves its counter part at
+ * zero.  After the call its first T*E*8 bytes hold the float64 logits
+ * [T, E].  Calls sharing a workspace must not run concurrently.  Other limits
+ * and errors as moe_route.
+ */
+size_t moe_route_gemv_workspace_bytes(int64_t T, int32_t num_experts);
+moe_status moe_route_gemv(const void* x, const float* gate_weight, const float* correction_bias, int64_t T,
+                          int32_t hidden, const moe_route_params* p, int32_t* topk_ids, float* topk_weights,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------- route + permute, no allocation
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
@@ -156,7 +179,13 @@ moe_status moe_route_permute_noalloc(const float* logits, const float* correctio
  * context and quality", Activations: E4M3 with a power-of-two scale per 32
  * values; "What makes it fast", speed v5.2: FP8 x FP4 block-scaled GEMMs).
  */
-typedef enum { MOE_FP4_MX = 0, MOE_FP4_NV = 1 } moe_fp4_format;
+/* MOE_FP4_MXC: compact MXFP4 storage at 4.125 bits per weight (moe_fp4_compact_mx
+ * writes it): the E2M1 codes unchanged, one 4-bit exponent code c per 32-value
+ * block (block 2i in the low nibble of scale byte i, so scale is u8 [E, n, k/64])
+ * and one power-of-two base 2^b per expert matrix in global_scale; the block's
+ * scale is 2^(b + c).  Runs the weight-streaming kernel only (MOE_ALGO_DECODE or
+ * AUTO) with BF16 or NVFP4 activations; needs k % 512 == 0. */
+typedef enum { MOE_FP4_MX = 0, MOE_FP4_NV = 1, MOE_FP4_MXC = 2 } moe_fp4_format;
 
 /* moe_fp4_weights.flags */
 #define MOE_FP4_SCALES_POW2 1 /* NV: every E4M3 scale byte is zero or a power of two (true of
@@ -184,8 +213,9 @@ typedef struct {
   int32_t n;                  /* output features (rows of each expert matrix) */
   int32_t k;                  /* input features; k % 128 == 0 */
   const uint8_t* packed;      /* codes [E, n, k/2] ("weight_packed")                    */
-  const uint8_t* scale;       /* MX: E8M0 [E, n, k/32] | NV: E4M3 [E, n, k/16]          */
-  const float* global_scale;  /* NV: float [E] (per expert matrix) | MX: NULL            */
+  const uint8_t* scale;       /* MX: E8M0 [E, n, k/32] | NV: E4M3 [E, n, k/16] | MXC: exponent
+                                 codes u8 [E, n, k/64]                                   */
+  const float* global_scale;  /* NV: float [E] (per expert matrix) | MXC: base 2^b [E] | MX: NULL */
   int32_t flags;              /* MOE_FP4_SCALES_POW2 | MOE_FP4_MX_EXACT (NV only) | MOE_FP4_TILED */
 } moe_fp4_weights;
 
@@ -199,7 +229,8 @@ typedef struct {
  *           64*s + 16*c + b of row 16t + r   (c < 4, r < 16, b < 16)
  *   scales: column window w (k 512w .. 512w+511) of tile t is a block of
  *           16*G bytes at (t * (k/512) + w) * 16*G; row 16t + r's G scale
- *           bytes of the window sit at G*r   (MX: G = 16 E8M0; NV: G = 32 E4M3)
+ *           bytes of the window sit at G*r   (MX: G = 16 E8M0; NV: G = 32 E4M3;
+ *           MXC: G = 8 bytes of exponent codes)
  * Global scales are unchanged.  Needs n % 16 == 0 and k % 512 == 0; the
  * outputs have the sizes of the inputs, must not overlap them and must be
  * 16-byte aligned.  num_experts == 0 is a no-op.
@@ -251,6 +282,12 @@ typedef struct {
                                  exactly the NVFP4 operand (W4A4 down projection)       */
   int32_t format;             /* MOE_OUT_*: MXFP8 and planes only from the MXFP8 /
                                  NVFP4-plane activation modes                             */
+  float* row_sumsq;           /* float [rows, n/64] or NULL (MOE_EPI_NONE, MFMA-tiled kernels
+                                 only: n % 256 == 0, k % 256 == 0, algo AUTO or PREFILL):
+                                 element [r, c] is the sum of squares of row r's FP32
+                                 outputs in columns 64c .. 64c+63, before any rounding --
+                                 the parts of the REAP saliency's output norm
+                                 (moe_reap_saliency_accumulate)                          */
 } moe_out;
 
 #define MOE_ALGO_AUTO 0       /* choose by rows per expert                                */
@@ -297,6 +334,27 @@ moe_status fp4_transcode_mx_to_nv(const uint8_t* mx_scale, const uint8_t* packed
                                   int32_t n, int32_t k, uint8_t* nv_scale, float* global_scale,
                                   int64_t* counters, hipStream_t stream);
 
+/* --------------------------------------------------------- compact storage
+ * MXFP4 -> compact storage (format MOE_FP4_MXC), 4.125 bits per weight.
+ * "MiMo-V2.6-Flash-MOPD on one RTX PRO 6000" ("What makes it fast", speed v4)
+ * stores the experts in a lossless compact encoding of 4.125 bits per weight;
+ * the page gives the size, not the layout -- this one is the library's: per
+ * matrix, b = (largest finite block exponent) - 15 (b = 0 if there is none),
+ * global_base = 2^b, and each E8M0 2^e becomes the 4-bit code e - b.  Codes
+ * below 0 are written as 0: counted in counters[1] when all 32 codes of the
+ * block are +-0 (exact), else in counters[2] (re-rounded, not exact); E8M0 NaN
+ * (0xFF) becomes 15, counted in counters[3]; counters[0] = number of blocks.
+ * The encoding is exact when counters[2] and counters[3] are zero, and a GEMM
+ * on it then gives bit-for-bit the MXFP4 result.  The counters are zeroed by
+ * the call.  Codes unchanged: the compact weights reuse `packed`.
+ *   mx_scale u8 [M, n, k/32]; packed u8 [M, n, k/2] (read only, for the
+ *   all-zero test); exp_codes u8 [M, n, k/64]; global_base float [M];
+ *   counters int64 [4].  k % 512 == 0, n % 16 == 0, buffers 16-byte aligned.
+ */
+moe_status moe_fp4_compact_mx(const uint8_t* mx_scale, const uint8_t* packed, int64_t num_mats, int32_t n,
+                              int32_t k, uint8_t* exp_codes, float* global_base, int64_t* counters,
+                              hipStream_t stream);
+
 /* --------------------------------------------------- NVFP4 quantisation
  * Per row and 16-element block of bf16 x: s = E4M3_rne(max|x| / (6 g)) saturated
  * at 448, codes = E2M1_rne(x / (s g)) saturated at +-6 with the sign of x
@@ -308,6 +366,26 @@ moe_status fp4_transcode_mx_to_nv(const uint8_t* mx_scale, const uint8_t* packed
  */
 moe_status moe_quantize_nvfp4(const void* x, int64_t rows, int32_t k, float input_scale,
                               uint8_t* codes, uint8_t* scales, void* dequant, hipStream_t stream);
+
+/* ----------------------------------------------------- REAP saliency
+ * REAP expert saliency ("MiMo-V2.6-Flash -- REAP-50" card, "Pruning Method":
+ * S_j = mean over the tokens t routed to expert j of g_{t,j} times the L2 norm
+ * of expert j's output for t), accumulated over batches:
+ *   saliency_sum[e] += sum over e's permuted rows r of
+ *                      topk_weights[sorted_slots[r]] * sqrt(sum_c row_sumsq[r, c])
+ *   counts[e]       += number of e's rows
+ * in float64, rows in order and parts in order (deterministic); S_e =
+ * saliency_sum[e] / counts[e].  g is the weight the combine applies (the
+ * normalised top-k weight x routed_scaling_factor); row_sumsq comes from the
+ * down projection's moe_out.row_sumsq (parts = n / 64).
+ *   row_sumsq float [rows, parts]; expert_offsets int32 [E+1]; sorted_slots
+ *   int32 [rows]; topk_weights float [T * top_k] (slot order); saliency_sum
+ *   double [E]; counts int64 [E].  rows == 0 or E == 0 is a no-op.
+ */
+moe_status moe_reap_saliency_accumulate(const float* row_sumsq, int64_t rows, int32_t parts,
+                                        const int32_t* expert_offsets, int32_t num_experts,
+                                        const int32_t* sorted_slots, const float* topk_weights, double* saliency_sum,
+                                        int64_t* counts, hipStream_t stream);
 
 /* ---------------------------------------------------- MXFP8 quantisation
  * W4A8 activations ("MiMo-V2.6-Flash-MOPD on one RTX PRO 6000", "Quantization,

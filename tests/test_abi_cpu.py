@@ -158,3 +158,31 @@ def test_route_permute_noalloc_rejects_before_touching_the_gpu():
     _err(f(FAKE, None, 4, ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, None), moe.MOE_ERR_INVALID)
     too_many = (1 << 27) // (256 * 8) + 1
     _err(f(FAKE, None, too_many, ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None), moe.MOE_ERR_UNSUPPORTED)
+
+
+def test_compact_format_checks():
+    """Compact (MXC) weights: base scales required, k % 512, weight-streaming
+    kernel only; the converter checks sizes, pointers and alignment."""
+    act = moe.Act(moe.MOE_ACT_BF16, 0x40000, None, 1.0, None, 1, 8)
+    G = ctypes.c_void_p(0x70000)
+    wc = moe.Fp4Weights(moe.MOE_FP4_MXC, 4, 256, 512, 0x10000, 0x20000, G)
+    _err(_gemm(act, _w(fmt=moe.MOE_FP4_MXC), _w(fmt=moe.MOE_FP4_MXC)), moe.MOE_ERR_INVALID)   # no base
+    w640 = moe.Fp4Weights(moe.MOE_FP4_MXC, 4, 256, 640, 0x10000, 0x20000, G)
+    _err(_gemm(act, w640, w640), moe.MOE_ERR_UNSUPPORTED)                        # k % 512
+    _err(_gemm(act, wc, wc, algo=moe.MOE_ALGO_PREFILL), moe.MOE_ERR_UNSUPPORTED)
+    mx8 = moe.Act(moe.MOE_ACT_MXFP8, 0x40000, 0x50000, 1.0, None, 1, 8)
+    _err(_gemm(mx8, wc, wc), moe.MOE_ERR_UNSUPPORTED)                            # block-scaled MFMA modes
+    sq = moe.Out(0x30000, None, None, 1.0, None, 0, 0x60000)
+    _err(_gemm(act, wc, None, epi=moe.MOE_EPI_NONE, out=sq), moe.MOE_ERR_UNSUPPORTED)   # row_sumsq
+    flagged = moe.Fp4Weights(moe.MOE_FP4_MXC, 4, 256, 512, 0x10000, 0x20000, G, moe.MOE_FP4_SCALES_POW2)
+    _err(_gemm(act, flagged, flagged), moe.MOE_ERR_INVALID)                      # NV-only flags
+    assert _gemm(act, wc, wc, rows=0) == moe.MOE_OK
+    c = moe.lib.moe_fp4_compact_mx
+    cnt = ctypes.c_void_p(0x60000)
+    _err(c(FAKE, FAKE, 2, 256, 640, FAKE, FAKE, cnt, None), moe.MOE_ERR_INVALID)     # k % 512
+    _err(c(FAKE, FAKE, 2, 250, 512, FAKE, FAKE, cnt, None), moe.MOE_ERR_INVALID)     # n % 16
+    _err(c(FAKE, FAKE, 2, 256, 512, FAKE, FAKE, None, None), moe.MOE_ERR_INVALID)    # counters
+    _err(c(FAKE, None, 2, 256, 512, FAKE, FAKE, cnt, None), moe.MOE_ERR_INVALID)     # NULL
+    _err(c(ctypes.c_void_p(0x10008), FAKE, 2, 256, 512, FAKE, FAKE, cnt, None), moe.MOE_ERR_INVALID)
+    _err(moe.lib.moe_fp4_tile_weights(moe.MOE_FP4_MXC, 2, 256, 640, FAKE, FAKE, FAKE, FAKE, None),
+         moe.MOE_ERR_INVALID)

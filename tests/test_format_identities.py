@@ -86,3 +86,29 @@ def test_plane_values_against_oracle_dequant():
     lo = c * (2 * ((m >> 1) & 1) + (m & 1)) / 4.0
     got = (hi + lo) * np.ldexp(1.0, k - 1)
     assert np.array_equal(got, want)
+
+
+def e2m3_grid():
+    """E2M3 (FP6): sign, 2 exponent bits (bias 1), 3 mantissa bits, no specials."""
+    vals = set()
+    for e in range(4):
+        for m in range(8):
+            v = Fraction(m, 8) if e == 0 else Fraction(2) ** (e - 1) * (1 + Fraction(m, 8))
+            vals.update((v, -v))
+    return vals
+
+
+def test_two_fp6_planes_cannot_hold_every_nvfp4_value():
+    """Why the planes are E4M3 and not E2M3 (which the scaled MFMA would run at
+    the FP6 rate): for 44 of the 126 non-zero E4M3 scales s there is no power of
+    two S for which every c * s / S (c over the E2M1 values) is a sum of two
+    E2M3 values, so two FP6 planes under one shared scale cannot be exact."""
+    grid = e2m3_grid()
+    sums = {a + b for a in grid for b in grid}
+    none = []
+    for sb in range(1, 0x7F):
+        s = Fraction(oracle.e4m3_value(sb).item())
+        if not any(all(c * s / Fraction(2) ** a in sums for c in E2M1) for a in range(-40, 40)):
+            none.append(sb)
+    assert len(none) == 44
+    assert 0x7D in none                 # 416 = 2^8 * 1.625

@@ -1,0 +1,104 @@
+"""GPU parity of the fused router (router matmul + group top-k in one launch)
+against the oracle's float64 router matmul and routing, through the C ABI.
+
+ids exactly on every token (and no token of these workloads has a decision
+within 1e-12 of a tie), weights to rtol 1e-6, the float64 logits within the
+float64 summation bound of the oracle's, and the hand-off counters left zero.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import dev_bf16, dev_f32, host, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import block_scaled_fp4_group_amd as moe  # noqa: E402
+
+CASES = [("tiny", 32, False), ("tiny", 5, False), ("decode", 1, False), ("decode", 8, False), ("decode", 64, False),
+         ("decode", 67, False), ("prefill", 8192, True), ("reap50", 4096, False)]
+
+
+@pytest.mark.parametrize("name,T,with_bias", CASES)
+def test_route_gemv_parity(name, T, with_bias):
+    w = synth.WORKLOADS[name]
+    s = w.shape
+    say(f"route_gemv {name} T={T}")
+    x = synth.activations(w, T)
+    W = synth.router_weight(w)
+    bias = synth.correction_bias(w) if with_bias else None
+    r, l_ref = oracle.route_hidden(x, W, bias, s.n_group, s.topk_group, s.top_k, s.routed_scaling_factor)
+    ws = torch.zeros(moe.route_gemv_workspace_bytes(T, s.num_experts), dtype=torch.uint8, device="cuda")
+    xd, Wd, bd = dev_bf16(x), dev_f32(W), None if bias is None else dev_f32(bias)
+    for rep in range(2):                       # the counters must be back at zero for the second call
+        ids, wts = moe.route_gemv(xd, Wd, bd, s.num_experts, s.n_group, s.topk_group, s.top_k,
+                                  s.routed_scaling_factor, ws)
+        torch.cuda.synchronize()
+        say(f"  rep {rep}: near-ties flagged {int(r.near_tie.sum())}")
+        assert not r.near_tie.any()
+        assert np.array_equal(host(ids), r.ids)
+        np.testing.assert_allclose(host(wts), r.weights, rtol=1e-6)
+        wsh = host(ws)
+        n = T * s.num_experts
+        logits = wsh[:n * 8].view(np.float64).reshape(T, s.num_experts)
+        mag = oracle.bf16_value(x).__abs__() @ np.abs(W.astype(np.float64)).T
+        bound = 2 * s.hidden * 2.0 ** -53 * mag
+        assert np.all(np.abs(logits - l_ref) <= bound)
+        cstart = (n * 8 + 255) // 256 * 256
+        assert not wsh[cstart:].any(), "hand-off counters not left at zero"
+
+
+def test_route_gemv_rejects():
+    w = synth.WORKLOADS["decode"]
+    s = w.shape
+    x = torch.zeros((4, 768), dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros((256, 768), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(moe.route_gemv_workspace_bytes(4, 256), dtype=torch.uint8, device="cuda")
+    with pytest.raises(moe.MoeError) as ei:                 # hidden must be a multiple of 512
+        moe.route_gemv(x, W, None, 256, 8, 4, 8, 2.827, ws)
+    assert ei.value.status == moe.MOE_ERR_INVALID
+    x = torch.zeros((4, 4096), dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros((256, 4096), dtype=torch.float32, device="cuda")
+    with pytest.raises(moe.MoeError) as ei:
+        moe.route_gemv(x, W, None, 256, 8, 4, 8, 2.827, ws[:16])
+    assert ei.value.status == moe.MOE_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("T", [1, 64])
+def test_decode_layer_with_fused_router(T):
+    """The decode layer run from hidden states alone (router matmul fused with
+    the top-k, then the permutation): routing, permutation and y against the
+    oracle on the same float64 logits."""
+    w = synth.WORKLOADS["decode"]
+    s = w.shape
+    from test_gpu_layer import upload_weights, ExpertCache
+    W = synth.expert_weights(w)
+    dw = upload_weights(W, "mx")
+    x = synth.activations(w, T)
+    RW = synth.router_weight(w)
+    layer = moe.MoELayer(dw, s.num_experts, s.n_group, s.topk_group, s.top_k, s.routed_scaling_factor, T,
+                         router_weight=dev_f32(RW))
+    y = layer.forward(dev_bf16(x), None)
+    torch.cuda.synchronize()
+    r, l64 = oracle.route_hidden(x, RW, None, s.n_group, s.topk_group, s.top_k, s.routed_scaling_factor)
+    assert not r.near_tie.any()
+    assert np.array_equal(host(layer.ids[:T]), r.ids)
+    off, ss, sr = oracle.permute(r.ids, s.num_experts)
+    assert np.array_equal(host(layer.offsets), off)
+    assert np.array_equal(host(layer.sorted_slots[:T * s.top_k]), ss)
+    # the expert FFNs and combine on the oracle's routing of the same logits
+    cache = ExpertCache(W, "mx")
+    toks = np.arange(min(T, 4))
+    o = np.zeros((len(toks), s.top_k, s.hidden))
+    for i, t in enumerate(toks):
+        for j in range(s.top_k):
+            wg, wu, wd = cache(int(r.ids[t, j]))
+            _, o[i, j] = oracle.expert_ffn(x[t:t + 1], wg, wu, wd)
+    y64 = oracle.combine_f64(o, r.weights[toks])
+    from gpu_util import assert_close_rms, bf16_to_f64, host_bf16_bits
+    assert_close_rms(bf16_to_f64(host_bf16_bits(y)[toks]), y64, what="y (end-to-end, literal)")
