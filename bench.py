@@ -548,13 +548,13 @@ def run_compact(moe, synth, args):
 def run_tsweep(moe, synth, args):
     """Both GEMM kernels forced at each batch (decode weights, tiled): the
     token counts where the MFMA-tiled kernel overtakes the weight-streaming one
-    (MOE_ALGO_AUTO switches at rows >= 32 E, i.e. 1024 tokens at 256 experts)."""
+    (MOE_ALGO_AUTO switches at rows >= 8 E, i.e. 256 tokens at 256 experts and top-8)."""
     import torch
     wd = synth.WORKLOADS["decode"]
     s = wd.shape
     lw = make_weights(host_weights(synth, "decode", 0))
     res = {}
-    for T in (128, 256, 512, 768, 1024, 1536, 2048, 4096):
+    for T in (64, 128, 192, 256, 384, 512, 1024, 2048, 4096):
         x, l = dev_bf16(synth.activations(wd, T)), dev(synth.logits(wd, T))
         ly = layer_for(moe, lw, s, T)
         row = {}

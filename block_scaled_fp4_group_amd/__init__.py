@@ -152,10 +152,10 @@ def route_gemv_workspace_bytes(T: int, num_experts: int) -> int:
 def route_gemv(x: torch.Tensor, gate_weight: torch.Tensor, bias: Optional[torch.Tensor], num_experts: int,
                n_group: int, topk_group: int, top_k: int, routed_scaling_factor: float, workspace: torch.Tensor,
                norm_topk_prob: bool = True, ids=None, weights=None, stream=None):
-    """Router matmul (bf16 x, FP32 gate_weight [E, hidden], float64 sums) and
-    group top-k in one launch.  ``workspace``: uint8 of at least
-    route_gemv_workspace_bytes(T, E), zeroed before its first use; after the
-    call its first T*E*8 bytes hold the float64 logits."""
+    """Router matmul (bf16 x, FP32 gate_weight [E, hidden], float64 sums), then
+    the group top-k on its logits.  ``workspace``: uint8 of at least
+    route_gemv_workspace_bytes(T, E); after the call its first T*E*8 bytes hold
+    the float64 logits."""
     _dev(x, "x")
     _dev(gate_weight, "gate_weight")
     T, H = x.shape

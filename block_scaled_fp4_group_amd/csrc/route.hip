@@ -262,7 +262,8 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
                weights);
 }
 
-// Router and permutation in one launch (R = T * top_k <= kPermChunk).  Each
+// Router and permutation in one launch (R = T * top_k <= kPermChunk).  A
+// single block (T <= 4) routes and permutes with no hand-off.  Otherwise each
 // block routes its tokens, then adds one to *counter; the block that brings
 // it to gridDim.x has every block's ids behind it and runs the permutation,
 // then sets the counter back to zero for the next launch.  The fences are
@@ -282,6 +283,16 @@ __global__ __launch_bounds__(256) void route_permute_kernel(const float* __restr
   __shared__ int s_last;
   route_tokens(logits, bias, (int64_t)blockIdx.x * kRouteWaves, T, E, n_group, topk_group, top_k, scale, norm, ids,
                weights);
+  if (gridDim.x == 1) {
+    // one block routes every token: the ids it reads back are its own stores,
+    // so workgroup-scope ordering suffices (no device-scope cache write-back or
+    // invalidation, no counter)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    permute_one_chunk(ids, T * top_k, E, nbits, offsets, sorted_slots, slot_rows);
+    return;
+  }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // each wave, after its own stores
   __syncthreads();
   if (threadIdx.x == 0) s_last = atomicAdd(counter, 1u) == gridDim.x - 1;
@@ -305,35 +316,36 @@ moe_status launch_route(const float* logits, const float* bias, int64_t T, const
 bool route_permute_fits(int64_t T, int top_k) { return T >= 1 && T * top_k <= kPermChunk; }
 
 // ------------------------------------------------- router matmul + top-k
-// The router's matmul and the group top-k in one launch ("MiMo-V2.6-Flash-MOPD
-// on one RTX PRO 6000", "What makes it fast": one matmul and a fused top-k
-// per layer; "MiMo-V2.6-Flash-RL Mixed-Quant GGUF", "Quantization targets":
-// routers stay F32).  logits[t, e] = sum_k x[t, k] W[e, k] for bf16 x and the
-// FP32 weight W: each product is exact in float64 and the sum is float64, in a
-// fixed order, so the selection sees the oracle's float64 logits up to the
-// order of one float64 summation.
-//   * workgroup (b, q) of 16 waves: a 16-token x 16-expert tile (tokens 16q..,
-//     experts 16b..); wave w takes the w-th sixteenth of the hidden dimension
-//     and runs float64 16x16x4 MFMAs over it, each lane group g of the wave
-//     supplying a contiguous quarter of that range (the k of one MFMA is one
-//     value from each lane group), so every lane reads contiguous 16-byte
-//     pieces of its token row and expert row;
-//   * the 16 partial tiles meet in LDS and are added in wave order;
-//   * the workgroups of one 16-token block count themselves in counters[q]
-//     after a device-scope release; the last one (every logit of its tokens is
-//     then behind an acquire) routes the 16 tokens, one per wave, and sets the
-//     counter back to zero.
+// The router's matmul, then the group top-k on its float64 logits ("MiMo-
+// V2.6-Flash-MOPD on one RTX PRO 6000", "What makes it fast": one router
+// matmul and a fused top-k per layer; "MiMo-V2.6-Flash-RL Mixed-Quant GGUF",
+// "Quantization targets": routers stay F32).  logits[t, e] = sum_k x[t, k]
+// W[e, k] for bf16 x and the FP32 weight W: each product is exact in float64
+// and the sum is float64, in a fixed order, so the selection sees the
+// oracle's float64 logits up to the order of one float64 summation.  Two
+// launches on the caller's stream: a hand-off inside one launch (a device-
+// scope release by every workgroup and an acquire by the last, i.e. an L2
+// write-back per workgroup and an L2 invalidation) measured slower than the
+// kernel boundary.
+//   * T > 16 or hidden != 4096: workgroup (b, q) of 16 waves computes a
+//     16-token x 16-expert tile (tokens 16q.., experts 16b..); wave w takes the
+//     w-th sixteenth of the hidden dimension and runs float64 16x16x4 MFMAs
+//     over it, each lane group g of the wave supplying a contiguous quarter of
+//     that range (the k of one MFMA is one value from each lane group), so
+//     every lane reads contiguous 16-byte pieces of its token row and expert
+//     row; the 16 partial tiles meet in LDS and are added in wave order.
 constexpr int kGemvWaves = 16;
 constexpr int kGemvTile = 16;
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
+// KG: values per lane group known at compile time (64 for hidden 4096, so the
+// whole loop unrolls and every load is in flight before the first MFMA), or 0.
+template <int KG>
 __global__ __launch_bounds__(kGemvWaves * 64) void route_gemv_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ W, const float* __restrict__ bias, int64_t T, int H, int E,
-    int n_group, int topk_group, int top_k, float scale, int norm, int32_t* __restrict__ ids,
-    float* __restrict__ weights, double* __restrict__ logits, uint32_t* __restrict__ counters) {
+    const uint16_t* __restrict__ x, const float* __restrict__ W, int64_t T, int H, int E,
+    double* __restrict__ logits) {
   __shared__ double part[kGemvWaves][kGemvTile * kGemvTile];
-  __shared__ int s_last;
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
@@ -341,11 +353,11 @@ __global__ __launch_bounds__(kGemvWaves * 64) void route_gemv_kernel(
   const int e0 = blockIdx.x * kGemvTile;
   const int64_t t = min(t0 + r, T - 1);                       // rows past the end reread the last one
   const int e = min(e0 + r, E - 1);
-  const int kg = H / (kGemvWaves * 4);                         // values per lane group (a multiple of 8)
+  const int kg = KG > 0 ? KG : H / (kGemvWaves * 4);          // values per lane group (a multiple of 8)
   const uint16_t* xr = x + t * H + (int64_t)(wv * 4 + g) * kg;
   const float* wr = W + (int64_t)e * H + (int64_t)(wv * 4 + g) * kg;
   f64x4 acc = {0.0, 0.0, 0.0, 0.0};
-  for (int m = 0; m < kg; m += 8) {
+  auto chunk = [&](int m) {
     const u32x4 xv = *(const u32x4*)(xr + m);
     const f32x4 w0 = *(const f32x4*)(wr + m);
     const f32x4 w1 = *(const f32x4*)(wr + m + 4);
@@ -358,6 +370,12 @@ __global__ __launch_bounds__(kGemvWaves * 64) void route_gemv_kernel(
     acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_hi(xv[2]), (double)w1[1], acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_lo(xv[3]), (double)w1[2], acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_hi(xv[3]), (double)w1[3], acc, 0, 0, 0);
+  };
+  if constexpr (KG > 0) {
+#pragma unroll
+    for (int m = 0; m < KG; m += 8) chunk(m);
+  } else {
+    for (int m = 0; m < kg; m += 8) chunk(m);
   }
   // the float64 16x16x4 MFMA leaves D[token g + 4 i][expert r] in lane (r, g), element i (measured)
 #pragma unroll
@@ -371,19 +389,86 @@ __global__ __launch_bounds__(kGemvWaves * 64) void route_gemv_kernel(
     const int ee = e0 + threadIdx.x % kGemvTile;
     if (tt < T && ee < E) logits[tt * E + ee] = sum;
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // each wave, after its own stores
+}
+
+// Small batches (T <= 16, hidden 4096): workgroups of 16 waves over 8 experts
+// each.  Wave w takes the w-th sixteenth of the hidden dimension; lane l takes
+// expert l / 8 of the workgroup and the (l % 8)-th eighth of the wave's range,
+// so it reads 32 contiguous weights and the same range of each token row (four
+// tokens at a time), the loads issued before the first product.  Each lane sums its products in
+// order in float64, the eight lanes of an expert are added by a butterfly
+// (the same result in each), and the 16 wave sums are added in wave order in
+// LDS.
+constexpr int kGemvSmallE = 8;        // experts per workgroup
+
+constexpr int kGemvSmallH = 4096;
+
+template <int TT>
+__global__ __launch_bounds__(1024) void route_gemv_small_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ W, int T, int H, int E, double* __restrict__ logits) {
+  __shared__ double part[kGemvWaves][kGemvSmallE][TT];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int el = lane >> 3, q = lane & 7;
+  const int e = min((int)blockIdx.x * kGemvSmallE + el, E - 1);
+  constexpr int kq = kGemvSmallH / (kGemvWaves * kGemvSmallE);   // 32 values per lane
+  const int64_t k0 = (int64_t)wv * (H / kGemvWaves) + (int64_t)q * kq;
+  const float* wr = W + (int64_t)e * H + k0;
+  // tokens in groups of 4 (the loads of one group in flight at once)
+  for (int tg = 0; tg < TT; tg += 4) {
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    {
+      f32x4 w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] = *(const f32x4*)(wr + 4 * i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (TT == 1 && j > 0) break;
+        const uint16_t* xr = x + (int64_t)min(tg + j, T - 1) * H + k0;
+        u32x4 xv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xv[i] = *(const u32x4*)(xr + 8 * i);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t lo = xv[i >> 1][2 * (i & 1)], hi = xv[i >> 1][2 * (i & 1) + 1];
+          acc[j] = fma((double)bf16_lo(lo), (double)w[i][0], acc[j]);
+          acc[j] = fma((double)bf16_hi(lo), (double)w[i][1], acc[j]);
+          acc[j] = fma((double)bf16_lo(hi), (double)w[i][2], acc[j]);
+          acc[j] = fma((double)bf16_hi(hi), (double)w[i][3], acc[j]);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[j] += __shfl_xor(acc[j], 1, kWave);
+      acc[j] += __shfl_xor(acc[j], 2, kWave);
+      acc[j] += __shfl_xor(acc[j], 4, kWave);
+      if (q == 0 && tg + j < TT) part[wv][el][tg + j] = acc[j];
+    }
+  }
   __syncthreads();
-  if (threadIdx.x == 0) s_last = atomicAdd(&counters[blockIdx.y], 1u) == gridDim.x - 1;
-  __syncthreads();
-  if (!s_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  route_tokens<double, kGemvWaves>(logits, bias, t0, T, E, n_group, topk_group, top_k, scale, norm, ids, weights);
-  if (threadIdx.x == 0) atomicExch(&counters[blockIdx.y], 0u);
+  if (threadIdx.x < kGemvSmallE * T) {
+    const int t = threadIdx.x / kGemvSmallE, ee = threadIdx.x % kGemvSmallE;
+    double sum = 0.0;
+#pragma unroll
+    for (int w = 0; w < kGemvWaves; ++w) sum += part[w][ee][t];
+    const int eo = blockIdx.x * kGemvSmallE + ee;
+    if (eo < E) logits[(int64_t)t * E + eo] = sum;
+  }
+}
+
+// the group top-k of moe_route on the float64 logits, one wave per token
+__global__ __launch_bounds__(256) void route_f64_kernel(const double* __restrict__ logits,
+                                                        const float* __restrict__ bias, int64_t T, int E,
+                                                        int n_group, int topk_group, int top_k, float scale,
+                                                        int norm, int32_t* __restrict__ ids,
+                                                        float* __restrict__ weights) {
+  route_tokens(logits, bias, (int64_t)blockIdx.x * kRouteWaves, T, E, n_group, topk_group, top_k, scale, norm, ids,
+               weights);
 }
 
 size_t route_gemv_ws_bytes(int64_t T, int E) {
-  const size_t lg = ((size_t)T * (size_t)E * sizeof(double) + 255) & ~(size_t)255;
-  return lg + (size_t)((T + kGemvTile - 1) / kGemvTile) * sizeof(uint32_t);
+  return ((size_t)T * (size_t)E * sizeof(double) + 255) & ~(size_t)255;   // the float64 logits
 }
 
 moe_status launch_route_gemv(const void* x, const float* W, const float* bias, int64_t T, int H,
@@ -391,11 +476,23 @@ moe_status launch_route_gemv(const void* x, const float* W, const float* bias, i
   if (T == 0) return MOE_OK;
   const int E = p->num_experts;
   double* logits = (double*)ws;
-  uint32_t* counters = (uint32_t*)((uint8_t*)ws + (((size_t)T * (size_t)E * sizeof(double) + 255) & ~(size_t)255));
-  const dim3 grid((uint32_t)((E + kGemvTile - 1) / kGemvTile), (uint32_t)((T + kGemvTile - 1) / kGemvTile));
-  hipLaunchKernelGGL(route_gemv_kernel, grid, dim3(kGemvWaves * 64), 0, stream, (const uint16_t*)x, W, bias, T, H, E, p->n_group,
-                     p->topk_group, p->top_k, p->routed_scaling_factor, p->norm_topk_prob, ids, weights, logits,
-                     counters);
+  if (T <= kGemvTile && H == kGemvSmallH) {
+    auto small = T == 1   ? route_gemv_small_kernel<1>
+                 : T <= 4 ? route_gemv_small_kernel<4>
+                 : T <= 8 ? route_gemv_small_kernel<8>
+                          : route_gemv_small_kernel<16>;
+    hipLaunchKernelGGL(small, dim3((uint32_t)((E + kGemvSmallE - 1) / kGemvSmallE)), dim3(1024), 0, stream,
+                       (const uint16_t*)x, W, (int)T, H, E, logits);
+  } else {
+    const dim3 grid((uint32_t)((E + kGemvTile - 1) / kGemvTile), (uint32_t)((T + kGemvTile - 1) / kGemvTile));
+    hipLaunchKernelGGL(H == 4096 ? route_gemv_kernel<64> : route_gemv_kernel<0>, grid, dim3(kGemvWaves * 64), 0,
+                       stream, (const uint16_t*)x, W, T, H, E, logits);
+  }
+  const moe_status st = launch_status("moe_route_gemv");
+  if (st != MOE_OK) return st;
+  hipLaunchKernelGGL(route_f64_kernel, dim3((uint32_t)((T + kRouteWaves - 1) / kRouteWaves)), dim3(256), 0, stream,
+                     logits, bias, T, E, p->n_group, p->topk_group, p->top_k, p->routed_scaling_factor,
+                     p->norm_topk_prob, ids, weights);
   return launch_status("moe_route_gemv");
 }
 

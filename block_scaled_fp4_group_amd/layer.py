@@ -70,8 +70,8 @@ class MoELayer:
             self.row_sumsq = torch.empty((R, H // 64), dtype=torch.float32, device=dev)
             self.sal_sums = torch.zeros(E, dtype=torch.float64, device=dev)
             self.sal_counts = torch.zeros(E, dtype=torch.int64, device=dev)
-        if router_weight is not None:                           # fused router: logits + counters (left zero)
-            self.rws = torch.zeros(route_gemv_workspace_bytes(T, E), dtype=torch.uint8, device=dev)
+        if router_weight is not None:                           # router matmul: its float64 logits
+            self.rws = torch.empty(route_gemv_workspace_bytes(T, E), dtype=torch.uint8, device=dev)
         self.o = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
         self.y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         if act_mode == "mxfp8" or (act_mode == "nvfp4" and a_mode == "planes"):

@@ -122,10 +122,11 @@ moe_status moe_route_permute(const float* logits, const float* correction_bias, 
                              hipStream_t stream);
 
 /* ------------------------------------------------ router matmul + route
- * The router's matmul and the group top-k of moe_route in one launch ("MiMo-
- * V2.6-Flash-MOPD on one RTX PRO 6000", "What makes it fast": one matmul and a
- * fused top-k per layer; "MiMo-V2.6-Flash-RL Mixed-Quant GGUF", "Quantization
- * targets": the router weight stays F32).
+ * The router's matmul, then the group top-k of moe_route on its float64
+ * logits, as two launches on `stream` ("MiMo-V2.6-Flash-MOPD on one RTX PRO
+ * 6000", "What makes it fast": one matmul and a fused top-k per layer;
+ * "MiMo-V2.6-Flash-RL Mixed-Quant GGUF", "Quantization targets": the router
+ * weight stays F32).
  *   logits[t, e] = sum_k x[t, k] * gate_weight[e, k], each product of a bf16
  *   and an FP32 value exact in float64, summed in float64 (fixed order); the
  *   selection and weights then follow moe_route on these float64 logits.
@@ -134,10 +135,9 @@ moe_status moe_route_permute(const float* logits, const float* correction_bias, 
  *   hidden % 512 == 0; T <= 1048560;
  *   x, gate_weight and workspace 16-byte aligned.
  * workspace: at least moe_route_gemv_workspace_bytes(T, E) bytes of device
- * memory, ZEROED before its first use; every call leaves its counter part at
- * zero.  After the call its first T*E*8 bytes hold the float64 logits
- * [T, E].  Calls sharing a workspace must not run concurrently.  Other limits
- * and errors as moe_route.
+ * memory (any contents); after the call its first T*E*8 bytes hold the
+ * float64 logits [T, E].  Calls sharing a workspace must not run
+ * concurrently.  Other limits and errors as moe_route.
  */
 size_t moe_route_gemv_workspace_bytes(int64_t T, int32_t num_experts);
 moe_status moe_route_gemv(const void* x, const float* gate_weight, const float* correction_bias, int64_t T,
@@ -290,7 +290,7 @@ typedef struct {
                                  (moe_reap_saliency_accumulate)                          */
 } moe_out;
 
-#define MOE_ALGO_AUTO 0       /* choose by rows per expert                                */
+#define MOE_ALGO_AUTO 0       /* PREFILL when rows >= 8 * num_experts (or row_sumsq), else DECODE */
 #define MOE_ALGO_DECODE 1     /* weight-streaming kernel (few rows per expert): one
                                  workgroup per (expert, block of output features)         */
 #define MOE_ALGO_PREFILL 2    /* LDS-tiled MFMA kernel (many rows per expert)             */

@@ -3,7 +3,7 @@ against the oracle's float64 router matmul and routing, through the C ABI.
 
 ids exactly on every token (and no token of these workloads has a decision
 within 1e-12 of a tie), weights to rtol 1e-6, the float64 logits within the
-float64 summation bound of the oracle's, and the hand-off counters left zero.
+float64 summation bound of the oracle's.
 """
 import numpy as np
 import pytest
@@ -20,8 +20,11 @@ if not torch.cuda.is_available():
 
 import block_scaled_fp4_group_amd as moe  # noqa: E402
 
-CASES = [("tiny", 32, False), ("tiny", 5, False), ("decode", 1, False), ("decode", 8, False), ("decode", 64, False),
-         ("decode", 67, False), ("prefill", 8192, True), ("reap50", 4096, False)]
+# T <= 16 runs the one-workgroup-per-expert kernel (1, <= 8 and <= 16 tokens per
+# thread), larger T the 16 x 16 MFMA tiles
+CASES = [("tiny", 32, False), ("tiny", 5, False), ("tiny", 3, False), ("decode", 1, False), ("decode", 8, False),
+         ("decode", 16, False), ("prefill", 13, True), ("decode", 64, False), ("decode", 67, False),
+         ("prefill", 8192, True), ("reap50", 4096, False)]
 
 
 @pytest.mark.parametrize("name,T,with_bias", CASES)
@@ -33,9 +36,9 @@ def test_route_gemv_parity(name, T, with_bias):
     W = synth.router_weight(w)
     bias = synth.correction_bias(w) if with_bias else None
     r, l_ref = oracle.route_hidden(x, W, bias, s.n_group, s.topk_group, s.top_k, s.routed_scaling_factor)
-    ws = torch.zeros(moe.route_gemv_workspace_bytes(T, s.num_experts), dtype=torch.uint8, device="cuda")
+    ws = torch.full((moe.route_gemv_workspace_bytes(T, s.num_experts),), 0xA5, dtype=torch.uint8, device="cuda")
     xd, Wd, bd = dev_bf16(x), dev_f32(W), None if bias is None else dev_f32(bias)
-    for rep in range(2):                       # the counters must be back at zero for the second call
+    for rep in range(2):                       # a second call on the same workspace
         ids, wts = moe.route_gemv(xd, Wd, bd, s.num_experts, s.n_group, s.topk_group, s.top_k,
                                   s.routed_scaling_factor, ws)
         torch.cuda.synchronize()
@@ -49,8 +52,6 @@ def test_route_gemv_parity(name, T, with_bias):
         mag = oracle.bf16_value(x).__abs__() @ np.abs(W.astype(np.float64)).T
         bound = 2 * s.hidden * 2.0 ** -53 * mag
         assert np.all(np.abs(logits - l_ref) <= bound)
-        cstart = (n * 8 + 255) // 256 * 256
-        assert not wsh[cstart:].any(), "hand-off counters not left at zero"
 
 
 def test_route_gemv_rejects():
