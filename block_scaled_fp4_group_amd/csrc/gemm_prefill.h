@@ -251,7 +251,16 @@ __device__ __forceinline__ void pf_compute(const uint8_t* st, const uint8_t* ss,
     for (int t = 0; t < 4; ++t)
       b[t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(sa + swz_a(wm * 64 + t * 16 + li, lg * 4 + s)));
   };
+  // weight group g of k-slot s, dequantised to bf16
+  auto cvt = [&](int s, int g) {
+    const float sc = s < 2 ? s_lo[g] : s_hi[g];
+    return WF == 2 ? fp4x8_to_bf16_general(wq[g][s], sc) : fp4x8_to_bf16_pow2(wq[g][s], sc);
+  };
   read_bt(bt[0], 0);
+  // the converts run one weight group ahead of the MFMAs that use them, in a
+  // register set of their own, so they issue while the matrix core works
+  bf16x8 af[2];
+  af[0] = cvt(0, 0);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     if (s < 3) {
@@ -264,10 +273,10 @@ __device__ __forceinline__ void pf_compute(const uint8_t* st, const uint8_t* ss,
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const float sc = s < 2 ? s_lo[g] : s_hi[g];
-      const bf16x8 af = WF == 2 ? fp4x8_to_bf16_general(wq[g][s], sc) : fp4x8_to_bf16_pow2(wq[g][s], sc);
+      const int i = s * 4 + g;
+      if (i + 1 < 16) af[(i + 1) & 1] = cvt((i + 1) >> 2, (i + 1) & 3);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc[g][t] = mfma16(af, bt[s & 1][t], acc[g][t]);
+      for (int t = 0; t < 4; ++t) acc[g][t] = mfma16(af[i & 1], bt[s & 1][t], acc[g][t]);
     }
   }
 }
