@@ -224,7 +224,9 @@ struct PfNoHook {
 // TL: the weight stage holds each 16-row group as one 1 KB tiled block (lane
 // (li, lg) at 16 * (16 lg + li)) instead of swizzled rows.
 // WREG: the weight codes come in registers (wreg[g]) instead of the LDS stage.
-template <int NMAT, int WF, bool TL, typename SH, bool WREG = false, typename Hook = PfNoHook>
+// RB: the 16-row token blocks that hold rows of the tile (the rest are padding:
+// no LDS reads, no MFMAs)
+template <int NMAT, int WF, bool TL, typename SH, bool WREG = false, int RB = 4, typename Hook = PfNoHook>
 __device__ __forceinline__ void pf_compute(const uint8_t* st, const uint8_t* ss, f32x4 (&acc)[4][4], int wm, int wn,
                                            int li, int lg, Hook&& hook = Hook(), const u32x4* wreg = nullptr) {
   constexpr bool W_NV = WF != 0;
@@ -248,7 +250,7 @@ __device__ __forceinline__ void pf_compute(const uint8_t* st, const uint8_t* ss,
   bf16x8 bt[2][4];
   auto read_bt = [&](bf16x8 (&b)[4], int s) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < RB; ++t)
       b[t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(sa + swz_a(wm * 64 + t * 16 + li, lg * 4 + s)));
   };
   // weight group g of k-slot s, dequantised to bf16
@@ -276,7 +278,7 @@ __device__ __forceinline__ void pf_compute(const uint8_t* st, const uint8_t* ss,
       const int i = s * 4 + g;
       if (i + 1 < 16) af[(i + 1) & 1] = cvt((i + 1) >> 2, (i + 1) & 3);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc[g][t] = mfma16(af[i & 1], bt[s & 1][t], acc[g][t]);
+      for (int t = 0; t < RB; ++t) acc[g][t] = mfma16(af[i & 1], bt[s & 1][t], acc[g][t]);
     }
   }
 }
@@ -463,48 +465,61 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_dma_kernel(GemmArgs p
       for (int q = 0; q < kDmaPerStep; ++q) issue_one(S_tag, kb, q);
     };
 
-    f32x4 acc[4][4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the tile's K loop, for RB token blocks of 16 rows that hold rows of the
+    // tile (a 64-row tile of an expert's last rows often holds fewer than 64)
+    auto run = [&](auto RB_tag) {
+      constexpr int RB = decltype(RB_tag)::value;
+      f32x4 acc[4][4];
+  #pragma unroll
+      for (int g = 0; g < 4; ++g)
+  #pragma unroll
+        for (int t = 0; t < 4; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // step k from stage S: wait for this wave's loads of step k (those of step
-    // k + 1 may stay in flight), barrier (every wave's loads landed, every wave
-    // done with step k - 1), refill the stage of step k - 1 with step k + 2
-    // (past the end: step nk - 1 again, unread), compute
-    auto step = [&](auto S_tag, int k) {
-      constexpr int S = decltype(S_tag)::value;
-      __builtin_amdgcn_s_waitcnt((kDmaPerStep & 15) | (7 << 4) | (15 << 8));      // vmcnt(kDmaPerStep)
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      const int kn = min(k + 2, nk - 1);
-      constexpr auto SN = std::integral_constant<int, (S + 2) % 3>();
-      // the next stage's loads go out between this step's MFMA slots (two per
-      // slot), so the load unit drains them while the matrix cores work
-      auto hook = [&](int s) {
-        if (2 * s < kDmaPerStep) issue_one(SN, kn, 2 * s);
-        if (2 * s + 1 < kDmaPerStep) issue_one(SN, kn, 2 * s + 1);
+      // step k from stage S: wait for this wave's loads of step k (those of step
+      // k + 1 may stay in flight), barrier (every wave's loads landed, every wave
+      // done with step k - 1), refill the stage of step k - 1 with step k + 2
+      // (past the end: step nk - 1 again, unread), compute
+      auto step = [&](auto S_tag, int k) {
+        constexpr int S = decltype(S_tag)::value;
+        __builtin_amdgcn_s_waitcnt((kDmaPerStep & 15) | (7 << 4) | (15 << 8));      // vmcnt(kDmaPerStep)
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        const int kn = min(k + 2, nk - 1);
+        constexpr auto SN = std::integral_constant<int, (S + 2) % 3>();
+        // the next stage's loads go out between this step's MFMA slots (two per
+        // slot), so the load unit drains them while the matrix cores work
+        auto hook = [&](int s) {
+          if (2 * s < kDmaPerStep) issue_one(SN, kn, 2 * s);
+          if (2 * s + 1 < kDmaPerStep) issue_one(SN, kn, 2 * s + 1);
+        };
+        // every wave computes, also on rows past the tile's end (their outputs
+        // are not stored): a branch here made the compiler drain every load in
+        // flight before each step's first LDS read, losing the two-step lead
+        pf_compute<NMAT, WF, TL, SH, WREG, RB>(pf_stage<S>(), pf_sstage<S>(), acc, wm, wn, li, lg, hook, wring[S]);
       };
-      // every wave computes, also on rows past the tile's end (their outputs
-      // are not stored): a branch here made the compiler drain every load in
-      // flight before each step's first LDS read, losing the two-step lead
-      pf_compute<NMAT, WF, TL, SH, WREG>(pf_stage<S>(), pf_sstage<S>(), acc, wm, wn, li, lg, hook, wring[S]);
+
+      __syncthreads();                                                 // previous tile done with the stages
+      issue(std::integral_constant<int, 0>(), 0);
+      issue(std::integral_constant<int, 1>(), min(1, nk - 1));
+      int kb = 0;
+      for (; kb + 3 <= nk; kb += 3) {
+        step(std::integral_constant<int, 0>(), kb);
+        step(std::integral_constant<int, 1>(), kb + 1);
+        step(std::integral_constant<int, 2>(), kb + 2);
+      }
+      if (kb < nk) step(std::integral_constant<int, 0>(), kb);
+      if (kb + 1 < nk) step(std::integral_constant<int, 1>(), kb + 1);
+      pf_epilogue<NMAT>(p, T, acc, wglob, wm, wn, li, lg);
     };
-
-    __syncthreads();                                                 // previous tile done with the stages
-    issue(std::integral_constant<int, 0>(), 0);
-    issue(std::integral_constant<int, 1>(), min(1, nk - 1));
-    int kb = 0;
-    for (; kb + 3 <= nk; kb += 3) {
-      step(std::integral_constant<int, 0>(), kb);
-      step(std::integral_constant<int, 1>(), kb + 1);
-      step(std::integral_constant<int, 2>(), kb + 2);
+    if constexpr (SH::BM == 64) {
+      const int rb = (T.mrows + 15) >> 4;                            // workgroup-uniform
+      if (rb >= 4) run(std::integral_constant<int, 4>());
+      else if (rb == 3) run(std::integral_constant<int, 3>());
+      else if (rb == 2) run(std::integral_constant<int, 2>());
+      else run(std::integral_constant<int, 1>());
+    } else {
+      run(std::integral_constant<int, 4>());
     }
-    if (kb < nk) step(std::integral_constant<int, 0>(), kb);
-    if (kb + 1 < nk) step(std::integral_constant<int, 1>(), kb + 1);
-
-    pf_epilogue<NMAT>(p, T, acc, wglob, wm, wn, li, lg);
   }
   // the last tile leaves its unread repeat loads in flight: let them land
   // before the workgroup's LDS is released
