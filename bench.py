@@ -307,7 +307,7 @@ def main():
                                        "hip_graph_ms_per_step": round(r["graph_ms"], 4),
                                        "hip_graph_tokens_per_s": round(Tx / (r["graph_ms"] / 1e3), 1),
                                        "distinct_experts": r["D"],
-                                       "layer_hbm_frac": round(b / (r["ms"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                                       "layer_hbm_frac": round(b / (r["graph_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                                        "gate_up_hbm_frac": round(gate_up_bytes(r["D"], Tx, s) / (r["gate_up_ms"] / 1e3)
                                                                  / 1e9 / HBM_PEAK_GBS, 4)}
             del r
@@ -548,7 +548,7 @@ def run_compact(moe, synth, args):
 def run_tsweep(moe, synth, args):
     """Both GEMM kernels forced at each batch (decode weights, tiled): the
     token counts where the MFMA-tiled kernel overtakes the weight-streaming one
-    (MOE_ALGO_AUTO switches at rows >= 8 E, i.e. 256 tokens at 256 experts and top-8)."""
+    (MOE_ALGO_AUTO switches at rows >= 4 E, i.e. 128 tokens at 256 experts and top-8)."""
     import torch
     wd = synth.WORKLOADS["decode"]
     s = wd.shape

@@ -346,9 +346,9 @@ moe_status moe_fp4_grouped_gemm(const moe_act* a, const moe_fp4_weights* w0, con
   if (wf == 3) return launch_gemm_decode(g, swiglu, wf, a_nv, rows, stream);
   int use = algo;
   // measured crossover (decode weights, 256 experts): the MFMA-tiled kernels win
-  // the layer from 8 rows per expert on average (2048 rows), the weight-streaming
+  // the layer from 4 rows per expert on average (1024 rows), the weight-streaming
   // kernel below it
-  if (use == MOE_ALGO_AUTO) use = (rows >= 8LL * g.E || out->row_sumsq) ? MOE_ALGO_PREFILL : MOE_ALGO_DECODE;
+  if (use == MOE_ALGO_AUTO) use = (rows >= 4LL * g.E || out->row_sumsq) ? MOE_ALGO_PREFILL : MOE_ALGO_DECODE;
   if (use == MOE_ALGO_PREFILL) return launch_gemm_prefill(g, swiglu, wf, a_nv, rows, stream);
   return launch_gemm_decode(g, swiglu, wf, a_nv, rows, stream);
 }

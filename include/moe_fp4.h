@@ -290,7 +290,7 @@ typedef struct {
                                  (moe_reap_saliency_accumulate)                          */
 } moe_out;
 
-#define MOE_ALGO_AUTO 0       /* PREFILL when rows >= 8 * num_experts (or row_sumsq), else DECODE */
+#define MOE_ALGO_AUTO 0       /* PREFILL when rows >= 4 * num_experts (or row_sumsq), else DECODE */
 #define MOE_ALGO_DECODE 1     /* weight-streaming kernel (few rows per expert): one
                                  workgroup per (expert, block of output features)         */
 #define MOE_ALGO_PREFILL 2    /* LDS-tiled MFMA kernel (many rows per expert)             */
