@@ -284,13 +284,30 @@ __global__ __launch_bounds__(256) void route_permute_kernel(const float* __restr
   route_tokens(logits, bias, (int64_t)blockIdx.x * kRouteWaves, T, E, n_group, topk_group, top_k, scale, norm, ids,
                weights);
   if (gridDim.x == 1) {
-    // one block routes every token: the ids it reads back are its own stores,
-    // so workgroup-scope ordering suffices (no device-scope cache write-back or
-    // invalidation, no counter)
+    // one block routes every token (R = T * top_k <= 64 slots): the ids it
+    // reads back are its own stores, so workgroup-scope ordering suffices (no
+    // device-scope cache write-back or invalidation, no counter), and the
+    // stable counting sort is a direct count per slot and per expert
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    permute_one_chunk(ids, T * top_k, E, nbits, offsets, sorted_slots, slot_rows);
+    __shared__ int s_ids[kRouteWaves * 16];
+    const int R = (int)T * top_k;
+    if (threadIdx.x < R) s_ids[threadIdx.x] = ids[threadIdx.x];
+    __syncthreads();
+    if (threadIdx.x < R) {
+      // row of slot j: slots of lower experts, then lower slots of the same expert
+      const int j = threadIdx.x, e = s_ids[j];
+      int row = 0;
+      for (int i = 0; i < R; ++i) row += (s_ids[i] < e || (s_ids[i] == e && i < j)) ? 1 : 0;
+      sorted_slots[row] = j;
+      slot_rows[j] = row;
+    }
+    for (int e = threadIdx.x; e <= E; e += blockDim.x) {
+      int c = 0;
+      for (int i = 0; i < R; ++i) c += s_ids[i] < e ? 1 : 0;
+      offsets[e] = c;
+    }
     return;
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // each wave, after its own stores
