@@ -573,13 +573,13 @@ def run_tsweep(moe, synth, args):
 def run_router(moe, synth, args):
     """Router matmul fused with the group top-k (moe_route_gemv) at decode
     batches, against the top-k alone on given logits (moe_route) and a torch
-    FP32 matmul (the unfused router's matmul)."""
+    FP32 matmul (the router matmul done by a library GEMM)."""
     import torch
     w = synth.WORKLOADS["decode"]
     RW = dev(synth.router_weight(w))
     res = {}
     for T in (1, 8, 64):
-        log(f"[bench] fused router T={T}")
+        log(f"[bench] router matmul + top-k T={T}")
         x, l = dev_bf16(synth.activations(w, T)), dev(synth.logits(w, T))
         ws = torch.zeros(moe.route_gemv_workspace_bytes(T, 256), dtype=torch.uint8, device="cuda")
         ids = torch.empty((T, 8), dtype=torch.int32, device="cuda")

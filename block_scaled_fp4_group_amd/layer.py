@@ -108,7 +108,7 @@ class MoELayer:
         R = T * self.top_k
         ids, topw = self.ids[:T], self.topw[:T]
         if logits is None:
-            # router matmul + top-k in one launch, then the permutation
+            # router matmul, its top-k, then the permutation
             route_gemv(x, self.router_weight, bias, self.E, self.n_group, self.topk_group, self.top_k, self.scale,
                        self.rws, True, ids=ids, weights=topw)
             permute(ids, self.E, workspace=self.ws, offsets=self.offsets, sorted_slots=self.sorted_slots[:R],

@@ -106,8 +106,9 @@ moe_status moe_permute(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_
  * for bit, as the two calls.  When T*top_k <= 2048 (every decode batch) both
  * run in one launch: each router workgroup counts itself in *counter after
  * writing its tokens' ids, and the last one to arrive runs the permutation,
- * then sets *counter back to zero.  Larger batches make the two separate
- * launches (workspace as for moe_permute; counter unused).
+ * then sets *counter back to zero (up to 4 tokens a single workgroup routes
+ * and permutes, and the counter is not touched).  Larger batches make the two
+ * separate launches (workspace as for moe_permute; counter unused).
  *   counter: one uint32 of device memory, 4-byte aligned, owned by the caller;
  *            zero before the first call, and every call leaves it zero.  Calls
  *            that share a counter must not run concurrently (same stream, or

@@ -1,4 +1,4 @@
-"""GPU parity of the fused router (router matmul + group top-k in one launch)
+"""GPU parity of the router matmul and its group top-k (moe_route_gemv)
 against the oracle's float64 router matmul and routing, through the C ABI.
 
 ids exactly on every token (and no token of these workloads has a decision
@@ -71,7 +71,7 @@ def test_route_gemv_rejects():
 
 
 @pytest.mark.parametrize("T", [1, 64])
-def test_decode_layer_with_fused_router(T):
+def test_decode_layer_with_router_matmul(T):
     """The decode layer run from hidden states alone (router matmul fused with
     the top-k, then the permutation): routing, permutation and y against the
     oracle on the same float64 logits."""

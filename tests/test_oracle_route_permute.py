@@ -179,7 +179,7 @@ def test_near_tie_flag_on_constructed_gaps(gap_expert, gap_group, flag):
     assert sorted({int(e) // 8 for e in r.ids[0]}) == [0, 1, 2, 3]
 
 
-# ------------------------------------------------ router matmul (fused router)
+# ------------------------------------------------ router matmul + top-k
 def test_router_logits_within_float64_sum_bound():
     """The float64 router matmul against exact rational dot products: every
     product bf16 x FP32 is exact, so the only error is the float64 summation,
