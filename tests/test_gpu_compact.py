@@ -189,3 +189,56 @@ def test_compact_gemm_rejects_prefill_only_requests():
     assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
     with pytest.raises(ValueError):
         moe.compact_weights(moe.tile_weights(w))
+
+
+@pytest.fixture(scope="module")
+def decode_layer_weights():
+    """Decode-shape weights in the tiled layout: MXFP4, and the same in compact storage."""
+    from test_gpu_layer import upload_weights
+    dw = upload_weights(synth.expert_weights(synth.WORKLOADS["decode"]), "mx")
+    mx = moe.LayerWeights(*(moe.tile_weights(getattr(dw, n)) for n in ("gate", "up", "down")))
+    cw = []
+    for n in ("gate", "up", "down"):
+        c, cnt = moe.compact_weights(getattr(dw, n))
+        torch.cuda.synchronize()
+        assert list(host(cnt)[1:]) == [0, 0, 0]
+        cw.append(moe.tile_weights(c))
+    return mx, moe.LayerWeights(*cw)
+
+
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_compact_decode_layer_is_bitwise_mx(decode_layer_weights, T):
+    """The whole decode layer (route, permute, both GEMMs, combine) on compact
+    tiled weights gives the bytes of the layer on the MXFP4 weights, from a HIP
+    graph replayed with new inputs (eager work between the replays)."""
+    w = synth.WORKLOADS["decode"]
+    s = w.shape
+    mx, cw = decode_layer_weights
+    mk = lambda lw: moe.MoELayer(lw, s.num_experts, s.n_group, s.topk_group, s.top_k, s.routed_scaling_factor, T)
+    lay_mx, lay_c = mk(mx), mk(cw)
+    x_static = dev_bf16(synth.activations(w, T))
+    l_static = torch.from_numpy(synth.logits(w, T)).cuda()
+    y_static = torch.empty((T, s.hidden), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        lay_c.forward(x_static, l_static, y=y_static)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        lay_c.forward(x_static, l_static, y=y_static)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(29)
+    for rep in range(3):
+        say(f"compact layer T={T} rep={rep}")
+        xb = synth.bf16_bits_from_f32(rng.standard_normal((T, s.hidden)).astype(np.float32))
+        lg = rng.standard_normal((T, s.num_experts)).astype(np.float32)
+        x_new, l_new = dev_bf16(xb), torch.from_numpy(lg).cuda()
+        x_static.copy_(x_new)
+        l_static.copy_(l_new)
+        graph.replay()
+        torch.cuda.synchronize()
+        y_mx = host_bf16_bits(lay_mx.forward(x_new, l_new)).copy()
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bf16_bits(y_static), y_mx), f"replay {rep}: compact layer differs from MXFP4"

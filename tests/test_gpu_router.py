@@ -103,3 +103,43 @@ def test_decode_layer_with_router_matmul(T):
     y64 = oracle.combine_f64(o, r.weights[toks])
     from gpu_util import assert_close_rms, bf16_to_f64, host_bf16_bits
     assert_close_rms(bf16_to_f64(host_bf16_bits(y)[toks]), y64, what="y (end-to-end, literal)")
+
+
+@pytest.mark.parametrize("T", [1, 64])
+def test_router_layer_hip_graph(T):
+    """The decode layer with the router matmul captured in a HIP graph: every
+    replay (new hidden states copied into the captured buffer, eager work and
+    synchronisations between replays) gives the bytes of an eager forward."""
+    w = synth.WORKLOADS["decode"]
+    s = w.shape
+    from test_gpu_layer import upload_weights
+    dw = upload_weights(synth.expert_weights(w), "mx")
+    RW = dev_f32(synth.router_weight(w))
+    mk = lambda: moe.MoELayer(dw, s.num_experts, s.n_group, s.topk_group, s.top_k, s.routed_scaling_factor, T,
+                              router_weight=RW)
+    layer, eager = mk(), mk()
+    x_static = dev_bf16(synth.activations(w, T))
+    y_static = torch.empty((T, s.hidden), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.forward(x_static, None, y=y_static)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer.forward(x_static, None, y=y_static)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(17)
+    from gpu_util import host_bf16_bits
+    for rep in range(4):
+        say(f"router graph replay T={T} rep={rep}")
+        xb = synth.bf16_bits_from_f32(rng.standard_normal((T, s.hidden)).astype(np.float32))
+        x_new = dev_bf16(xb)
+        x_static.copy_(x_new)
+        graph.replay()
+        torch.cuda.synchronize()
+        y_ref = host_bf16_bits(eager.forward(x_new, None)).copy()
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bf16_bits(y_static), y_ref), f"replay {rep} differs from eager"
+        assert np.array_equal(host(layer.ids[:T]), host(eager.ids[:T]))
