@@ -186,3 +186,32 @@ def test_compact_format_checks():
     _err(c(ctypes.c_void_p(0x10008), FAKE, 2, 256, 512, FAKE, FAKE, cnt, None), moe.MOE_ERR_INVALID)
     _err(moe.lib.moe_fp4_tile_weights(moe.MOE_FP4_MXC, 2, 256, 640, FAKE, FAKE, FAKE, FAKE, None),
          moe.MOE_ERR_INVALID)
+
+
+def test_header_is_plain_c():
+    """include/moe_fp4.h compiles as C99 in a C translation unit (no C++ or
+    torch types cross the boundary) and links against the library."""
+    import shutil
+    import subprocess
+    import tempfile
+    gcc = shutil.which("gcc")
+    hip_inc = "/opt/rocm/include"
+    if gcc is None or not os.path.isdir(hip_inc):
+        pytest.skip("needs gcc and the HIP headers")
+    src = ("#include \"moe_fp4.h\"\n"
+           "int main(void) {\n"
+           "  moe_fp4_weights w = {MOE_FP4_MXC, 1, 16, 512, 0, 0, 0, 0};\n"
+           "  moe_route_params p = {256, 8, 4, 8, 2.827f, 1};\n"
+           "  (void)w; (void)p;\n"
+           "  return moe_status_string(MOE_OK) ? 0 : 1;\n"
+           "}\n")
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "use.c")
+        with open(c, "w") as f:
+            f.write(src)
+        out = os.path.join(d, "use")
+        r = subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__", "-I",
+                            os.path.join(ROOT, "include"), "-I", hip_inc, c, "-o", out, moe.LIB_PATH,
+                            "-Wl,-rpath," + os.path.dirname(moe.LIB_PATH), "-Wl,--allow-shlib-undefined"],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
