@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const uint16_t* _
   }
   u32x4 o;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+  for (int i = 0; i < 4; ++i) o[i] = cvt_bf16x2(acc[2 * i], acc[2 * i + 1]);
   *(u32x4*)(y + t * h + c) = o;
 }
 

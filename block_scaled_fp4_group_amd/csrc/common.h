@@ -25,7 +25,7 @@ moe_status launch_status(const char* what);
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// float -> bf16 bits, round to nearest even (finite inputs)
+// float -> bf16 bits, round to nearest even (finite inputs), in integer ops
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
@@ -33,6 +33,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 }
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+}
+// the same rounding with the gfx950 packed convert: one instruction for the
+// pair (the MFMA kernels' epilogues; the weight-streaming kernel keeps the
+// integer form, with which the compiler schedules it better)
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
 // --------------------------------------------------------- scale decoders

@@ -99,7 +99,14 @@ __device__ __forceinline__ bool find_active_expert(const int32_t* __restrict__ o
   return r1 > r0;
 }
 
-__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+// g * sigmoid(g) with the hardware reciprocal (1 ulp) instead of a correctly
+// rounded division: about half the instructions of the MFMA kernels' SwiGLU
+// epilogues
+__device__ __forceinline__ float silu_f(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+// the division form, kept by the weight-streaming kernel: with the shorter
+// epilogue the compiler interleaved the next tile's work into it, which took
+// more registers and measured 3.8% slower at 64 tokens
+__device__ __forceinline__ float silu_div(float g) { return g / (1.0f + __expf(-g)); }
 
 // compute units of the current device (persistent grids: one workgroup per CU)
 inline int device_cus() {

@@ -243,7 +243,7 @@ __device__ __forceinline__ void decode_finish(const GemmArgs& p, const f32x4 (&a
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float g = acc[0][i] * wglob[0];
-    v[i] = NMAT == 2 ? silu_f(g) * (acc[NMAT - 1][i] * wglob[NMAT - 1]) : g;
+    v[i] = NMAT == 2 ? silu_div(g) * (acc[NMAT - 1][i] * wglob[NMAT - 1]) : g;
   }
   const uint32_t b01 = pack_bf16x2(v[0], v[1]), b23 = pack_bf16x2(v[2], v[3]);
   const int col = nt0 + 4 * lg;

@@ -158,7 +158,7 @@ __device__ __forceinline__ void sx_epilogue(const GemmArgs& p, const PfTile& T, 
         const float g = acc[gp][t][i];
         v[i] = NMAT == 2 ? silu_f(g) * acc[gp + 2][t][i] : g;
       }
-      const uint32_t b01 = pack_bf16x2(v[0], v[1]), b23 = pack_bf16x2(v[2], v[3]);
+      const uint32_t b01 = cvt_bf16x2(v[0], v[1]), b23 = cvt_bf16x2(v[2], v[3]);
       const int col = T.nbase + (NMAT == 2 ? wn * 32 : wn * 64) + gp * 16 + 4 * lg;
       if (p.out_bf16 && ok) *(u32x2*)(p.out_bf16 + ro * N + col) = u32x2{b01, b23};
       r[gp][0] = bf16_lo(b01);

@@ -2,10 +2,13 @@
 the oracle, on shapes that give every persistent workgroup several tiles.
 
 The persistent kernels walk a tile list (expert, n-tile, m-tile) cut into one
-contiguous slice per XCD; a workgroup restarts its load pipeline on each new
-tile.  These shapes make 1,000-1,600 tiles for 256 workgroups (4-6 tiles each),
-with ragged experts (tails of every length, empty experts) so that slice
-boundaries fall inside experts.  Each case is checked on every row:
+contiguous slice per XCD.  The bf16-token 64 x 512 kernel at these sizes
+(~700 rows per expert) carries its load pipeline from each tile into the
+next (the next tile's first steps load during the current tile's last ones);
+the others restart it on each tile.  These shapes make 1,000-1,600 tiles for
+256 workgroups (4-6 tiles each), with ragged experts (tails of every length,
+empty experts) so that slice boundaries fall inside experts.  Each case is
+checked on every row:
   * bf16 tokens, 64 x 512 tiles (SwiGLU gate/up and down), row-major and tiled;
   * bf16 tokens, 128 x 256 tiles (N a multiple of 256 but not 512);
   * NVFP4 tokens (codes + scales dequantised in the kernel), 128 x 256 tiles.
@@ -155,3 +158,57 @@ def test_tall_bf16_tiles_every_row():
         zref = bf16_to_f64(oracle.round_to_bf16_bits(oracle.silu(a @ dg[e].T) * (a @ du[e].T)))
         assert_close_rms(zb[r0:r1], zref, what=f"z expert {e}", ulp_rel=BF16_ULP)
         assert_close_rms(ob[r0:r1], zv[r0:r1] @ dd[e].T, what=f"o expert {e}", ulp_rel=BF16_ULP)
+
+
+def _pad_experts(w, extra):
+    """The same weights with `extra` all-zero experts appended (never read: no rows)."""
+    pad = lambda t: torch.cat([t, torch.zeros((extra,) + tuple(t.shape[1:]), dtype=t.dtype, device=t.device)])
+    return moe.Weights(pad(w.packed), pad(w.scale))
+
+
+@pytest.mark.parametrize("swiglu", [True, False])
+def test_cross_tile_kernel_equals_per_tile_kernel(swiglu):
+    """bf16 tokens on 64 x 512 tiles run one of two kernels: with at least 160
+    rows per expert on average the pipeline runs on across tiles, below that it
+    restarts per tile (and skips the empty 16-row blocks of a tile).  Both add
+    the same products in the same order, so the same call with 128 more empty
+    experts (the average falls below 160 rows) gives the same bytes; the rows
+    are also checked against the oracle."""
+    H, I = 2048, 1024
+    counts = _counts(4, 700)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offsets[-1])
+    extra = 128
+    assert R >= 160 * E and R < 160 * (E + extra)
+    offsets2 = np.concatenate([offsets, np.full(extra, R)]).astype(np.int32)
+    say(f"cross-tile vs per-tile swiglu={swiglu} R={R}")
+    if swiglu:
+        tsrc = 4096
+        x = synth.random_bf16(231, (tsrc, H))
+        gather = np.random.default_rng(232).integers(0, tsrc * 8, size=R).astype(np.int32)
+        wg0, dg = _weights(233, I, H, False)
+        wu0, du = _weights(234, I, H, False)
+        wg, wu = moe.tile_weights(wg0), moe.tile_weights(wu0)
+        wg2, wu2 = moe.tile_weights(_pad_experts(wg0, extra)), moe.tile_weights(_pad_experts(wu0, extra))
+        args = dict(gather=dev_i32(gather), gather_div=8, algo=moe.MOE_ALGO_PREFILL)
+        y1 = moe.grouped_gemm(dev_bf16(x), wg, wu, dev_i32(offsets), R, **args)
+        y2 = moe.grouped_gemm(dev_bf16(x), wg2, wu2, dev_i32(offsets2), R, **args)
+        a_all = bf16_to_f64(x)[gather // 8]
+        ref = lambda e, r0, r1: bf16_to_f64(oracle.round_to_bf16_bits(
+            oracle.silu(a_all[r0:r1] @ dg[e].T) * (a_all[r0:r1] @ du[e].T)))
+    else:
+        zin = synth.random_bf16(235, (R, I))
+        wd0, dd = _weights(236, H, I, False)
+        wd, wd2 = moe.tile_weights(wd0), moe.tile_weights(_pad_experts(wd0, extra))
+        y1 = moe.grouped_gemm(dev_bf16(zin), wd, None, dev_i32(offsets), R, algo=moe.MOE_ALGO_PREFILL)
+        y2 = moe.grouped_gemm(dev_bf16(zin), wd2, None, dev_i32(offsets2), R, algo=moe.MOE_ALGO_PREFILL)
+        zv = bf16_to_f64(zin)
+        ref = lambda e, r0, r1: zv[r0:r1] @ dd[e].T
+    torch.cuda.synchronize()
+    b1, b2 = host_bf16_bits(y1), host_bf16_bits(y2)
+    assert np.array_equal(b1, b2), f"{int(np.sum(b1 != b2))} outputs differ between the two kernels"
+    yv = bf16_to_f64(b1)
+    for e in range(E):
+        r0, r1 = offsets[e], offsets[e + 1]
+        if r1 > r0:
+            assert_close_rms(yv[r0:r1], ref(e, r0, r1), what=f"expert {e} ({r1 - r0} rows)", ulp_rel=BF16_ULP)
