@@ -604,6 +604,57 @@ __device__ __forceinline__ PfTile locate_tile_lds(const int* s_pref, const int2*
   return t;
 }
 
+// bf16 output through LDS: each wave's outputs (64 token rows x 64 columns,
+// SwiGLU 32) go to LDS in the MFMA layout (8 bytes per lane and 16-row group)
+// and come back as whole rows, so each global store writes 8 (16) rows of 128
+// (64) contiguous bytes instead of 16 rows of 32.  (The down projection's 64
+// KB of output per tile, stored in 32-byte pieces, took 11% of its time,
+// partly by slowing the next steps' loads.)  The staging area is stage 3's
+// token buffer, idle between the tile's last step and the next tile's first
+// (which refills it): 2 KB per wave, one 16-row group at a time.  16-byte
+// chunk c of row r sits at chunk c ^ (r mod chunks-per-row).
+template <int NMAT>
+__device__ __forceinline__ void xt_epilogue_bf16(const GemmArgs& p, const PfTile& T, const f32x4 (&acc)[4][4],
+                                                 const float (&wglob)[NMAT], int wn, int li, int lg, uint8_t* ob) {
+  constexpr int RBY = NMAT == 2 ? 64 : 128;                  // bytes per output row of the wave
+  constexpr int CPR = RBY / 16;                              // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;                              // rows per read-back instruction
+  const int N = p.N;
+  const int lane = threadIdx.x & 63;
+  const int col0 = T.nbase + (NMAT == 2 ? wn * 32 : wn * 64);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    float sq = 0.0f;
+#pragma unroll
+    for (int gp = 0; gp < (NMAT == 2 ? 2 : 4); ++gp) {
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float g = acc[gp][t][i] * wglob[0];
+        v[i] = NMAT == 2 ? silu_f(g) * (acc[gp + 2][t][i] * wglob[NMAT - 1]) : g;
+        if (NMAT == 1) sq = fmaf(v[i], v[i], sq);
+      }
+      const int cb = gp * 32 + lg * 8;                       // byte of the row: columns gp * 16 + 4 lg ..
+      *(u32x2*)(ob + li * RBY + (((cb >> 4) ^ (li & (CPR - 1))) << 4) + (cb & 15)) =
+          u32x2{cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3])};
+    }
+    if (NMAT == 1 && p.out_sumsq) {
+      // lanes li + 16 lg hold the 4 x 4 columns of each group: add the four lane groups in a fixed order
+      const float s1 = sq + __shfl_xor(sq, 16, kWave);
+      const float s2 = s1 + __shfl_xor(s1, 32, kWave);
+      if (t * 16 + li < T.mrows && lg == 0) p.out_sumsq[(T.rbase + t * 16 + li) * (N / 64) + col0 / 64] = s2;
+    }
+    // (the LDS operations of one wave complete in order: the reads see the writes, the next group's writes
+    // follow the reads)
+#pragma unroll
+    for (int r0 = 0; r0 < 16; r0 += RPI) {
+      const int row = r0 + lane / CPR, c = lane % CPR;
+      const u32x4 d = *(const u32x4*)(ob + row * RBY + ((c ^ (row & (CPR - 1))) << 4));
+      if (t * 16 + row < T.mrows) *(u32x4*)(p.out_bf16 + (T.rbase + t * 16 + row) * N + col0 + c * 8) = d;
+    }
+  }
+}
+
 template <int NMAT, int WF, bool TL>
 __global__ __launch_bounds__(kPfThreads) void gemm_prefill_xt_kernel(GemmArgs p) {
   using SH = PfWide;
@@ -611,6 +662,7 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_xt_kernel(GemmArgs p)
   constexpr int kStages = 4;
   static_assert(kStages * (SH::AStage + SH::SStage) + (kPfMaxE + 1) * 12 + kPfThreads / kWave * 4 <= 160 * 1024,
                 "LDS");
+  static_assert(kPfThreads / kWave * 2048 <= SH::AStage, "epilogue staging: 2 KB per wave in one token stage");
   __shared__ int s_pref[kPfMaxE + 1];
   __shared__ int2 s_rng[kPfMaxE + 1];
   __shared__ int s_wc[kPfThreads / kWave];
@@ -802,7 +854,13 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_xt_kernel(GemmArgs p)
     // indices load during the epilogue
     pT = locate_tile_lds<NMAT, SH>(s_pref, s_rng, p.E, tile_at(i + 2));
     src_rows(pT, psrc);
-    pf_epilogue<NMAT>(p, cur.T, acc, wglob, 0, wn, li, lg);
+    if (p.out_bf16 && !p.out_codes && !p.out_dq) {                // bf16 out (+ row sums of squares)
+      // every wave done reading stage 3 (the last step's operands) before any overwrites it
+      __builtin_amdgcn_s_barrier();
+      xt_epilogue_bf16<NMAT>(p, cur.T, acc, wglob, wn, li, lg, px_stage<3>() + wv * 2048);
+    } else {
+      pf_epilogue<NMAT>(p, cur.T, acc, wglob, 0, wn, li, lg);
+    }
     cur = nx;
   }
   // the last tile leaves its unread repeat loads in flight: let them land
