@@ -612,13 +612,17 @@ __device__ __forceinline__ PfTile locate_tile_lds(const int* s_pref, const int2*
 // partly by slowing the next steps' loads.)  The staging area is stage 3's
 // token buffer, idle between the tile's last step and the next tile's first
 // (which refills it): 2 KB per wave, one 16-row group at a time.  16-byte
-// chunk c of row r sits at chunk c ^ (r mod chunks-per-row).
+// chunk c of row r sits at chunk c ^ (r / R256 mod chunks-per-row), R256 the
+// rows per 256 bytes: the 16 rows of an 8-byte write and the rows of a 16-byte
+// read then cover distinct banks.
 template <int NMAT>
 __device__ __forceinline__ void xt_epilogue_bf16(const GemmArgs& p, const PfTile& T, const f32x4 (&acc)[4][4],
                                                  const float (&wglob)[NMAT], int wn, int li, int lg, uint8_t* ob) {
   constexpr int RBY = NMAT == 2 ? 64 : 128;                  // bytes per output row of the wave
   constexpr int CPR = RBY / 16;                              // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;                              // rows per read-back instruction
+  constexpr int R256 = 256 / RBY;                            // rows per 256 bytes (one bank sweep)
+  auto slot = [](int row, int c) { return ((c ^ ((row / R256) & (CPR - 1))) << 4); };
   const int N = p.N;
   const int lane = threadIdx.x & 63;
   const int col0 = T.nbase + (NMAT == 2 ? wn * 32 : wn * 64);
@@ -635,8 +639,7 @@ __device__ __forceinline__ void xt_epilogue_bf16(const GemmArgs& p, const PfTile
         if (NMAT == 1) sq = fmaf(v[i], v[i], sq);
       }
       const int cb = gp * 32 + lg * 8;                       // byte of the row: columns gp * 16 + 4 lg ..
-      *(u32x2*)(ob + li * RBY + (((cb >> 4) ^ (li & (CPR - 1))) << 4) + (cb & 15)) =
-          u32x2{cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3])};
+      *(u32x2*)(ob + li * RBY + slot(li, cb >> 4) + (cb & 15)) = u32x2{cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3])};
     }
     if (NMAT == 1 && p.out_sumsq) {
       // lanes li + 16 lg hold the 4 x 4 columns of each group: add the four lane groups in a fixed order
@@ -649,7 +652,7 @@ __device__ __forceinline__ void xt_epilogue_bf16(const GemmArgs& p, const PfTile
 #pragma unroll
     for (int r0 = 0; r0 < 16; r0 += RPI) {
       const int row = r0 + lane / CPR, c = lane % CPR;
-      const u32x4 d = *(const u32x4*)(ob + row * RBY + ((c ^ (row & (CPR - 1))) << 4));
+      const u32x4 d = *(const u32x4*)(ob + row * RBY + slot(row, c));
       if (t * 16 + row < T.mrows) *(u32x4*)(p.out_bf16 + (T.rbase + t * 16 + row) * N + col0 + c * 8) = d;
     }
   }
