@@ -334,6 +334,60 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& p, const PfTile& T, 
   }
 }
 
+// bf16 output through LDS: each wave's outputs (64 token rows x 64 columns,
+// SwiGLU 32) go to LDS in the MFMA layout (8 bytes per lane and 16-row group)
+// and come back as whole rows, so each global store writes 8 (16) rows of 128
+// (64) contiguous bytes instead of 16 rows of 32.  (The down projection's 64
+// KB of output per tile, stored in 32-byte pieces, took 11% of its time,
+// partly by slowing the next steps' loads.)  The staging area is a token
+// stage that no load is filling (the last step's, after a barrier): 2 KB per
+// wave, one 16-row group at a time.  16-byte
+// chunk c of row r sits at chunk c ^ (r / R256 mod chunks-per-row), R256 the
+// rows per 256 bytes: the 16 rows of an 8-byte write and the rows of a 16-byte
+// read then cover distinct banks.
+template <int NMAT>
+__device__ __forceinline__ void pf_epilogue_staged(const GemmArgs& p, const PfTile& T, const f32x4 (&acc)[4][4],
+                                                 const float (&wglob)[NMAT], int wn, int li, int lg, uint8_t* ob) {
+  constexpr int RBY = NMAT == 2 ? 64 : 128;                  // bytes per output row of the wave
+  constexpr int CPR = RBY / 16;                              // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;                              // rows per read-back instruction
+  constexpr int R256 = 256 / RBY;                            // rows per 256 bytes (one bank sweep)
+  auto slot = [](int row, int c) { return ((c ^ ((row / R256) & (CPR - 1))) << 4); };
+  const int N = p.N;
+  const int lane = threadIdx.x & 63;
+  const int col0 = T.nbase + (NMAT == 2 ? wn * 32 : wn * 64);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    float sq = 0.0f;
+#pragma unroll
+    for (int gp = 0; gp < (NMAT == 2 ? 2 : 4); ++gp) {
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float g = acc[gp][t][i] * wglob[0];
+        v[i] = NMAT == 2 ? silu_f(g) * (acc[gp + 2][t][i] * wglob[NMAT - 1]) : g;
+        if (NMAT == 1) sq = fmaf(v[i], v[i], sq);
+      }
+      const int cb = gp * 32 + lg * 8;                       // byte of the row: columns gp * 16 + 4 lg ..
+      *(u32x2*)(ob + li * RBY + slot(li, cb >> 4) + (cb & 15)) = u32x2{cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3])};
+    }
+    if (NMAT == 1 && p.out_sumsq) {
+      // lanes li + 16 lg hold the 4 x 4 columns of each group: add the four lane groups in a fixed order
+      const float s1 = sq + __shfl_xor(sq, 16, kWave);
+      const float s2 = s1 + __shfl_xor(s1, 32, kWave);
+      if (t * 16 + li < T.mrows && lg == 0) p.out_sumsq[(T.rbase + t * 16 + li) * (N / 64) + col0 / 64] = s2;
+    }
+    // (the LDS operations of one wave complete in order: the reads see the writes, the next group's writes
+    // follow the reads)
+#pragma unroll
+    for (int r0 = 0; r0 < 16; r0 += RPI) {
+      const int row = r0 + lane / CPR, c = lane % CPR;
+      const u32x4 d = *(const u32x4*)(ob + row * RBY + slot(row, c));
+      if (t * 16 + row < T.mrows) *(u32x4*)(p.out_bf16 + (T.rbase + t * 16 + row) * N + col0 + c * 8) = d;
+    }
+  }
+}
+
 // ------------------------------------------------ bf16 tokens: direct to LDS
 // 64 x 512 tiles: weight codes in registers, not LDS (3-4% faster, although the
 // compiler then drains the loads in flight once per step before the first LDS read)
@@ -512,7 +566,15 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_dma_kernel(GemmArgs p
       }
       if (kb < nk) step(std::integral_constant<int, 0>(), kb);
       if (kb + 1 < nk) step(std::integral_constant<int, 1>(), kb + 1);
-      pf_epilogue<NMAT>(p, T, acc, wglob, wm, wn, li, lg);
+      if (NMAT == 1 && WF != 2 && SH::BM == 64 && p.out_bf16 && !p.out_codes && !p.out_dq) {
+        // the down projection's bf16 out through LDS (pf_epilogue_staged), staged in the last step's
+        // stage: the loads in flight (its repeats) fill the other two
+        __builtin_amdgcn_s_barrier();
+        uint8_t* ob = ((nk - 1) % 3 == 0 ? pf_stage<0>() : ((nk - 1) % 3 == 1 ? pf_stage<1>() : pf_stage<2>())) + wv * 2048;
+        pf_epilogue_staged<NMAT>(p, T, acc, wglob, wn, li, lg, ob);
+      } else {
+        pf_epilogue<NMAT>(p, T, acc, wglob, wm, wn, li, lg);
+      }
     };
     if constexpr (SH::BM == 64) {
       const int rb = (T.mrows + 15) >> 4;                            // workgroup-uniform
@@ -602,60 +664,6 @@ __device__ __forceinline__ PfTile locate_tile_lds(const int* s_pref, const int2*
   t.mrows = min(SH::BM, r1 - t.rbase);
   t.nbase = nt * (SH::BN / NMAT);
   return t;
-}
-
-// bf16 output through LDS: each wave's outputs (64 token rows x 64 columns,
-// SwiGLU 32) go to LDS in the MFMA layout (8 bytes per lane and 16-row group)
-// and come back as whole rows, so each global store writes 8 (16) rows of 128
-// (64) contiguous bytes instead of 16 rows of 32.  (The down projection's 64
-// KB of output per tile, stored in 32-byte pieces, took 11% of its time,
-// partly by slowing the next steps' loads.)  The staging area is stage 3's
-// token buffer, idle between the tile's last step and the next tile's first
-// (which refills it): 2 KB per wave, one 16-row group at a time.  16-byte
-// chunk c of row r sits at chunk c ^ (r / R256 mod chunks-per-row), R256 the
-// rows per 256 bytes: the 16 rows of an 8-byte write and the rows of a 16-byte
-// read then cover distinct banks.
-template <int NMAT>
-__device__ __forceinline__ void xt_epilogue_bf16(const GemmArgs& p, const PfTile& T, const f32x4 (&acc)[4][4],
-                                                 const float (&wglob)[NMAT], int wn, int li, int lg, uint8_t* ob) {
-  constexpr int RBY = NMAT == 2 ? 64 : 128;                  // bytes per output row of the wave
-  constexpr int CPR = RBY / 16;                              // 16-byte chunks per row
-  constexpr int RPI = 64 / CPR;                              // rows per read-back instruction
-  constexpr int R256 = 256 / RBY;                            // rows per 256 bytes (one bank sweep)
-  auto slot = [](int row, int c) { return ((c ^ ((row / R256) & (CPR - 1))) << 4); };
-  const int N = p.N;
-  const int lane = threadIdx.x & 63;
-  const int col0 = T.nbase + (NMAT == 2 ? wn * 32 : wn * 64);
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    float sq = 0.0f;
-#pragma unroll
-    for (int gp = 0; gp < (NMAT == 2 ? 2 : 4); ++gp) {
-      float v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float g = acc[gp][t][i] * wglob[0];
-        v[i] = NMAT == 2 ? silu_f(g) * (acc[gp + 2][t][i] * wglob[NMAT - 1]) : g;
-        if (NMAT == 1) sq = fmaf(v[i], v[i], sq);
-      }
-      const int cb = gp * 32 + lg * 8;                       // byte of the row: columns gp * 16 + 4 lg ..
-      *(u32x2*)(ob + li * RBY + slot(li, cb >> 4) + (cb & 15)) = u32x2{cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3])};
-    }
-    if (NMAT == 1 && p.out_sumsq) {
-      // lanes li + 16 lg hold the 4 x 4 columns of each group: add the four lane groups in a fixed order
-      const float s1 = sq + __shfl_xor(sq, 16, kWave);
-      const float s2 = s1 + __shfl_xor(s1, 32, kWave);
-      if (t * 16 + li < T.mrows && lg == 0) p.out_sumsq[(T.rbase + t * 16 + li) * (N / 64) + col0 / 64] = s2;
-    }
-    // (the LDS operations of one wave complete in order: the reads see the writes, the next group's writes
-    // follow the reads)
-#pragma unroll
-    for (int r0 = 0; r0 < 16; r0 += RPI) {
-      const int row = r0 + lane / CPR, c = lane % CPR;
-      const u32x4 d = *(const u32x4*)(ob + row * RBY + slot(row, c));
-      if (t * 16 + row < T.mrows) *(u32x4*)(p.out_bf16 + (T.rbase + t * 16 + row) * N + col0 + c * 8) = d;
-    }
-  }
 }
 
 template <int NMAT, int WF, bool TL>
@@ -860,7 +868,7 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_xt_kernel(GemmArgs p)
     if (p.out_bf16 && !p.out_codes && !p.out_dq) {                // bf16 out (+ row sums of squares)
       // every wave done reading stage 3 (the last step's operands) before any overwrites it
       __builtin_amdgcn_s_barrier();
-      xt_epilogue_bf16<NMAT>(p, cur.T, acc, wglob, wn, li, lg, px_stage<3>() + wv * 2048);
+      pf_epilogue_staged<NMAT>(p, cur.T, acc, wglob, wn, li, lg, px_stage<3>() + wv * 2048);
     } else {
       pf_epilogue<NMAT>(p, cur.T, acc, wglob, 0, wn, li, lg);
     }
