@@ -373,12 +373,22 @@ __global__ __launch_bounds__(kPfThreads) void gemm_scaled_kernel(GemmArgs p) {
     if (kb + 1 < nk) step(std::integral_constant<int, 1>(), kb + 1);
 
     if (p.out_format == MOE_OUT_NVFP4) {
-      // bf16 (and NVFP4) outputs: the shared epilogue; the global scales are
+      // bf16 (and NVFP4) outputs: the shared epilogues; the global scales are
       // already inside the E8M0 scales
       float wglob[NMAT];
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) wglob[m] = 1.0f;
-      pf_epilogue<NMAT>(p, T, acc, wglob, 0, wn, li, lg);
+      if (NMAT == 1 && !PL && p.out_bf16 && !p.out_codes && !p.out_dq) {
+        // the down projection's bf16 out through LDS (pf_epilogue_staged), staged in the last
+        // step's token stage: the loads in flight (its repeats) fill the other two.  (Not in the
+        // planes kernel, which already spills registers.)
+        static_assert(kPfThreads / kWave * 2048 <= kSxStageMax, "epilogue staging: 2 KB per wave");
+        __builtin_amdgcn_s_barrier();
+        uint8_t* ob = ((nk - 1) % 3 == 0 ? sx_stage<0>() : ((nk - 1) % 3 == 1 ? sx_stage<1>() : sx_stage<2>())) + wv * 2048;
+        pf_epilogue_staged<NMAT>(p, T, acc, wglob, wn, li, lg, ob);
+      } else {
+        pf_epilogue<NMAT>(p, T, acc, wglob, 0, wn, li, lg);
+      }
     } else {
       sx_epilogue<NMAT>(p, T, acc, wn, li, lg);
     }
