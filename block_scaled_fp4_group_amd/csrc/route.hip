@@ -116,11 +116,12 @@ static_assert(kPermThreads == 256, "the router block runs the permutation");
 
 // Wave wv routes token tb + wv; the logits are FP32 (the router output as
 // stored) or float64 (the fused router matmul's own sums).
+// s_ids (optional, LDS): the block's picks also go there, at [wv * top_k + r]
 template <typename LT, int NW = kRouteWaves>
 __device__ __forceinline__ void route_tokens(const LT* __restrict__ logits, const float* __restrict__ bias,
                                              int64_t tb, int64_t T, int E, int n_group, int topk_group, int top_k,
                                              float scale, int norm, int32_t* __restrict__ ids,
-                                             float* __restrict__ weights) {
+                                             float* __restrict__ weights, int* s_ids = nullptr) {
   __shared__ double gscore[NW][64];
   __shared__ double cval[NW][256];
   const int lane = threadIdx.x & 63;
@@ -250,6 +251,7 @@ __device__ __forceinline__ void route_tokens(const LT* __restrict__ logits, cons
     const double w = norm ? sel_s / tot * (double)scale : sel_s * (double)scale;
     ids[t * top_k + lane] = sel_e;
     weights[t * top_k + lane] = (float)w;
+    if (s_ids) s_ids[wv * top_k + lane] = sel_e;
   }
 }
 
@@ -281,20 +283,16 @@ __global__ __launch_bounds__(256) void route_permute_kernel(const float* __restr
                                                             int32_t* __restrict__ slot_rows,
                                                             uint32_t* __restrict__ counter) {
   __shared__ int s_last;
+  __shared__ int s_ids[kRouteWaves * 16];                      // top_k <= 16
   route_tokens(logits, bias, (int64_t)blockIdx.x * kRouteWaves, T, E, n_group, topk_group, top_k, scale, norm, ids,
-               weights);
+               weights, gridDim.x == 1 ? s_ids : nullptr);
   if (gridDim.x == 1) {
-    // one block routes every token (R = T * top_k <= 64 slots): the ids it
-    // reads back are its own stores, so workgroup-scope ordering suffices (no
-    // device-scope cache write-back or invalidation, no counter), and the
-    // stable counting sort is a direct count per slot and per expert
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    // one block routes every token (R = T * top_k <= 64 slots) and keeps its
+    // picks in LDS: no global round trip, no device-scope cache write-back or
+    // invalidation, no counter; the stable counting sort is a direct count
+    // per slot and per expert
     __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    __shared__ int s_ids[kRouteWaves * 16];
     const int R = (int)T * top_k;
-    if (threadIdx.x < R) s_ids[threadIdx.x] = ids[threadIdx.x];
-    __syncthreads();
     if (threadIdx.x < R) {
       // row of slot j: slots of lower experts, then lower slots of the same expert
       const int j = threadIdx.x, e = s_ids[j];
