@@ -71,6 +71,12 @@ def build(verbose: bool = True, jobs: int = 0) -> str:
     if rc != 0:
         sys.stderr.write("\n".join(msgs) + "\n")
         raise RuntimeError(f"link failed with exit code {rc}")
+    # a kernel template whose host-side instantiation clang silently drops
+    # leaves its launch stub undefined: the link succeeds and loading fails
+    undef = subprocess.run(["nm", "-u", tmp], capture_output=True, text=True).stdout
+    stubs = [l.split()[-1] for l in undef.splitlines() if "__device_stub__" in l]
+    if stubs:
+        raise RuntimeError("kernel launch stubs left undefined (host-side instantiation failed): " + ", ".join(stubs[:4]))
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB} from {len(srcs)} sources", flush=True)

@@ -95,43 +95,67 @@ __device__ __forceinline__ int nv_pow2_e8m0(uint32_t byte, float gmul) {
   return (int)((__float_as_uint(e4m3_to_f32(byte) * gmul) >> 23) & 0xFFu);
 }
 
-// One K step (128 values) from an LDS stage: 4 weight groups x 4 token groups
-// of 16 x 16, NH MFMA K-chunks each.  hook(s) runs before slot s's MFMAs.
-template <int NMAT, bool PL, bool W_NV, typename Hook>
+// One K step (128 values) from an LDS stage: 4 weight groups x RB token groups
+// of 16 x 16, NH MFMA K-chunks each (RB: the 16-row token groups that hold
+// rows of the tile; the rest are padding, with no LDS reads and no MFMAs).
+// hook(s), s < 4 NH, issues loads between the MFMAs, spread evenly.
+// The token operand of the next (chunk, token group) is read while the
+// current one's MFMAs run (two register sets), so the LDS latency overlaps
+// the matrix core.  Each token row's swizzle depends only on its row within
+// the 16-row group (sx_swz), so a lane's reads for all groups share one base
+// and differ by constant offsets.
+template <int NMAT, bool PL, bool W_NV, int RB, typename Hook>
 __device__ __forceinline__ void sx_compute(const uint8_t* st, const uint8_t* sws, f32x4 (&acc)[4][4], int wn, int li, int lg,
                                            const u32x4* wreg, const float* gmul, Hook&& hook) {
   using SH = SxShape<PL>;
-  const uint8_t* sa = st;
-  const uint8_t* sts = st + SH::AStage;
+  constexpr int NI = RB * SH::NH;                           // (chunk h, token group t < RB) in order
+  constexpr int NS = 4 * SH::NH;                            // hook slots, spread over the NI groups
+  const uint8_t* sa = st + li * SH::ARow;                   // this lane's row of token group 0
+  const uint8_t* sts = st + SH::AStage + li * 4 + lg;       // its token scale byte of group 0, chunk 0
+  uint32_t aoff[SH::NH][2];
 #pragma unroll
-  for (int h = 0; h < SH::NH; ++h) {
-    int wsc[4];
-    i32x8 wop[4];
-    const int blk = PL ? 2 * h + (lg >> 1) : lg;            // weight 32-block of this lane's K block
+  for (int h = 0; h < SH::NH; ++h)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int n = pf_lrow<NMAT, SH::BN>(wn, g) + li;      // block-local weight row
-      if (W_NV) wsc[g] = nv_pow2_e8m0(sws[n * 8 + 2 * blk], gmul[NMAT == 2 ? (g >> 1) : 0]);
-      else wsc[g] = sws[n * 4 + blk];
-      const u32x4 w = wreg[g];
-      // MXFP8: the lane's 32 codes; planes: its 16-block's 16 codes, twice
-      const u32x4 wv = PL ? (h == 0 ? u32x4{w[0], w[1], w[0], w[1]} : u32x4{w[2], w[3], w[2], w[3]}) : w;
-      // the FP4 operand occupies the low 4 dwords; the instruction does not read the others
-      wop[g] = __builtin_bit_cast(i32x8, __builtin_shufflevector(wv, wv, 0, 1, 2, 3, -1, -1, -1, -1));
+    for (int u = 0; u < 2; ++u) aoff[h][u] = 16u * (uint32_t)sx_swz<PL>(li, (PL ? 8 * h : 0) + lg + 4 * u);
+  i32x8 tb[2];
+  int tsc[2];
+  auto read_t = [&](int i) {
+    const int h = i / RB, t = i % RB;
+    const u32x4 b0 = *(const u32x4*)(sa + t * 16 * SH::ARow + aoff[h][0]);
+    const u32x4 b1 = *(const u32x4*)(sa + t * 16 * SH::ARow + aoff[h][1]);
+    tb[i & 1] = __builtin_bit_cast(i32x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+    tsc[i & 1] = sts[(PL ? h * 256 : 0) + t * 64];
+  };
+  int wsc[4];
+  i32x8 wop[4];
+  read_t(0);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int h = i / RB, t = i % RB;
+    if (t == 0) {
+      const int blk = PL ? 2 * h + (lg >> 1) : lg;          // weight 32-block of this lane's K block
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = pf_lrow<NMAT, SH::BN>(wn, g) + li;    // block-local weight row
+        if (W_NV) wsc[g] = nv_pow2_e8m0(sws[n * 8 + 2 * blk], gmul[NMAT == 2 ? (g >> 1) : 0]);
+        else wsc[g] = sws[n * 4 + blk];
+        const u32x4 w = wreg[g];
+        // MXFP8: the lane's 32 codes; planes: its 16-block's 16 codes, twice
+        const u32x4 wv = PL ? (h == 0 ? u32x4{w[0], w[1], w[0], w[1]} : u32x4{w[2], w[3], w[2], w[3]}) : w;
+        // the FP4 operand occupies the low 4 dwords; the instruction does not read the others
+        wop[g] = __builtin_bit_cast(i32x8, __builtin_shufflevector(wv, wv, 0, 1, 2, 3, -1, -1, -1, -1));
+      }
     }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int row = t * 16 + li;
-      const int c1 = (PL ? 8 * h : 0) + lg;
-      const u32x4 b0 = *(const u32x4*)(sa + row * SH::ARow + 16 * sx_swz<PL>(row, c1));
-      const u32x4 b1 = *(const u32x4*)(sa + row * SH::ARow + 16 * sx_swz<PL>(row, c1 + 4));
-      const int tsc = sts[(PL ? h * 256 : 0) + row * 4 + lg];
-      const i32x8 tb = __builtin_bit_cast(i32x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
-      hook(h * 4 + t);
+    if (i + 1 < NI) {
+      read_t(i + 1);
+      // keep the next group's reads above this group's MFMAs
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int g = 0; g < 4; ++g) acc[g][t] = mfma_fp4w_fp8t(wop[g], tb, acc[g][t], wsc[g], tsc);
     }
+#pragma unroll
+    for (int s = i * NS / NI; s < (i + 1) * NS / NI; ++s) hook(s);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) acc[g][t] = mfma_fp4w_fp8t(wop[g], tb[i & 1], acc[g][t], wsc[g], tsc[i & 1]);
   }
 }
 
@@ -247,6 +271,12 @@ __global__ __launch_bounds__(kPfThreads) void gemm_scaled_kernel(GemmArgs p) {
   const int64_t mat_scales = (int64_t)N * sc_row;
   const int a_row = PL ? 2 * K : K;                               // token operand bytes per row
   const int ts_row = PL ? K / 16 : K / 32;                        // token scale bytes per row
+  // every direct-to-LDS load is a buffer load: 32-bit lane offsets, the step's
+  // part uniform (64-bit global addresses cost two registers per load).  The
+  // token scales are a_bytes / 32 bytes in both modes (K/16 per 2K-byte plane
+  // row, K/32 per K-byte MXFP8 row).
+  const rsrc_t a_rsrc = make_rsrc(p.a_data, (uint32_t)min(p.a_bytes, (int64_t)0xffffffff));
+  const rsrc_t ts_rsrc = make_rsrc(p.a_scales, (uint32_t)min(p.a_bytes / 32, (int64_t)0xffffffff));
 
   for (int tile = t_begin; tile < t_end; tile += t_stride) {
     const PfTile T = locate_tile<NMAT, SH>(p, s_pref, tile);
@@ -320,15 +350,16 @@ __global__ __launch_bounds__(kPfThreads) void gemm_scaled_kernel(GemmArgs p) {
         }
       } else if (q < kW + kA) {
         const int i = q - kW;
-        __builtin_amdgcn_global_load_lds((const void*)(p.a_data + (int64_t)kb * SH::ARow + a_off[i]),
-                                         (lds_void_t*)(st + (wv * kA + i) * 1024), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void_t*)(st + (wv * kA + i) * 1024), 16, (int)a_off[i],
+                                                 (int)(kb * SH::ARow), 0, 0);
       } else if (q < kW + kA + kS) {
         const int h = q - kW - kA;
-        __builtin_amdgcn_global_load_lds((const void*)(s_base[h] + pf_scale_step<TL, W_NV>(kb) + s_off[h]),
-                                         (lds_void_t*)(sw_stage<S>() + (wv * kS + h) * 256), 4, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(s_base[h], (uint32_t)mat_scales),
+                                                 (lds_void_t*)(sw_stage<S>() + (wv * kS + h) * 256), 4, (int)s_off[h],
+                                                 (int)pf_scale_step<TL, W_NV>(kb), 0, 0);
       } else {
-        __builtin_amdgcn_global_load_lds((const void*)(p.a_scales + (int64_t)kb * SH::TSRow + ts_off),
-                                         (lds_void_t*)(st + SH::AStage + ts_half * 256), 4, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ts_rsrc, (lds_void_t*)(st + SH::AStage + ts_half * 256), 4, (int)ts_off,
+                                                 (int)(kb * SH::TSRow), 0, 0);
       }
     };
     auto issue = [&](auto S_tag, int kb) {
@@ -336,62 +367,73 @@ __global__ __launch_bounds__(kPfThreads) void gemm_scaled_kernel(GemmArgs p) {
       for (int q = 0; q < kDma; ++q) issue_one(S_tag, kb, q);
     };
 
-    f32x4 acc[4][4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the tile's K loop and epilogue for RB token groups of 16 rows that hold
+    // rows of the tile (an expert's last tile often holds fewer than 64)
+    auto run = [&](auto RB_tag) {
+      constexpr int RB = decltype(RB_tag)::value;
+      f32x4 acc[4][4];
+  #pragma unroll
+      for (int g = 0; g < 4; ++g)
+  #pragma unroll
+        for (int t = 0; t < 4; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // step k from stage S: this wave's loads of step k done (step k + 1's may
-    // be in flight), barrier (every wave's landed; every wave done with step
-    // k - 1), refill the stage of step k - 1 with step k + 2 between the MFMA
-    // slots (past the end: step nk - 1 again, unread), compute
-    auto step = [&](auto S_tag, int k) {
-      constexpr int S = decltype(S_tag)::value;
-      __builtin_amdgcn_s_waitcnt((kDma & 15) | (7 << 4) | (15 << 8));      // vmcnt(kDma)
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      const int kn = min(k + 2, nk - 1);
-      constexpr auto SN = std::integral_constant<int, (S + 2) % 3>();
-      auto hook = [&](int s) {
-        if (2 * s < kDma) issue_one(SN, kn, 2 * s);
-        if (2 * s + 1 < kDma) issue_one(SN, kn, 2 * s + 1);
-      };
-      sx_compute<NMAT, PL, W_NV>(sx_stage<S>(), sw_stage<S>(), acc, wn, li, lg, wring[S], gmul, hook);
-    };
-
-    __syncthreads();                                             // previous tile done with the stages
-    issue(std::integral_constant<int, 0>(), 0);
-    issue(std::integral_constant<int, 1>(), min(1, nk - 1));
-    int kb = 0;
-    for (; kb + 3 <= nk; kb += 3) {
-      step(std::integral_constant<int, 0>(), kb);
-      step(std::integral_constant<int, 1>(), kb + 1);
-      step(std::integral_constant<int, 2>(), kb + 2);
-    }
-    if (kb < nk) step(std::integral_constant<int, 0>(), kb);
-    if (kb + 1 < nk) step(std::integral_constant<int, 1>(), kb + 1);
-
-    if (p.out_format == MOE_OUT_NVFP4) {
-      // bf16 (and NVFP4) outputs: the shared epilogues; the global scales are
-      // already inside the E8M0 scales
-      float wglob[NMAT];
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m) wglob[m] = 1.0f;
-      if (NMAT == 1 && !PL && p.out_bf16 && !p.out_codes && !p.out_dq) {
-        // the down projection's bf16 out through LDS (pf_epilogue_staged), staged in the last
-        // step's token stage: the loads in flight (its repeats) fill the other two.  (Not in the
-        // planes kernel, which already spills registers.)
-        static_assert(kPfThreads / kWave * 2048 <= kSxStageMax, "epilogue staging: 2 KB per wave");
+      // step k from stage S: this wave's loads of step k done (step k + 1's may
+      // be in flight), barrier (every wave's landed; every wave done with step
+      // k - 1), refill the stage of step k - 1 with step k + 2 between the MFMA
+      // slots (past the end: step nk - 1 again, unread), compute
+      auto step = [&](auto S_tag, int k) {
+        constexpr int S = decltype(S_tag)::value;
+        __builtin_amdgcn_s_waitcnt((kDma & 15) | (7 << 4) | (15 << 8));      // vmcnt(kDma)
         __builtin_amdgcn_s_barrier();
-        uint8_t* ob = ((nk - 1) % 3 == 0 ? sx_stage<0>() : ((nk - 1) % 3 == 1 ? sx_stage<1>() : sx_stage<2>())) + wv * 2048;
-        pf_epilogue_staged<NMAT>(p, T, acc, wglob, wn, li, lg, ob);
-      } else {
-        pf_epilogue<NMAT>(p, T, acc, wglob, 0, wn, li, lg);
+        __builtin_amdgcn_sched_barrier(0);
+        const int kn = min(k + 2, nk - 1);
+        constexpr auto SN = std::integral_constant<int, (S + 2) % 3>();
+        auto hook = [&](int s) {
+          if (2 * s < kDma) issue_one(SN, kn, 2 * s);
+          if (2 * s + 1 < kDma) issue_one(SN, kn, 2 * s + 1);
+        };
+        sx_compute<NMAT, PL, W_NV, RB>(sx_stage<S>(), sw_stage<S>(), acc, wn, li, lg, wring[S], gmul, hook);
+      };
+
+      __syncthreads();                                             // previous tile done with the stages
+      issue(std::integral_constant<int, 0>(), 0);
+      issue(std::integral_constant<int, 1>(), min(1, nk - 1));
+      int kb = 0;
+      for (; kb + 3 <= nk; kb += 3) {
+        step(std::integral_constant<int, 0>(), kb);
+        step(std::integral_constant<int, 1>(), kb + 1);
+        step(std::integral_constant<int, 2>(), kb + 2);
       }
-    } else {
-      sx_epilogue<NMAT>(p, T, acc, wn, li, lg);
-    }
+      if (kb < nk) step(std::integral_constant<int, 0>(), kb);
+      if (kb + 1 < nk) step(std::integral_constant<int, 1>(), kb + 1);
+
+      if (p.out_format == MOE_OUT_NVFP4) {
+        // bf16 (and NVFP4) outputs: the shared epilogues; the global scales are
+        // already inside the E8M0 scales
+        float wglob[NMAT];
+  #pragma unroll
+        for (int m = 0; m < NMAT; ++m) wglob[m] = 1.0f;
+        if (NMAT == 1 && !PL && p.out_bf16 && !p.out_codes && !p.out_dq) {
+          // the down projection's bf16 out through LDS (pf_epilogue_staged), staged in the last
+          // step's token stage: the loads in flight (its repeats) fill the other two.  (Not in the
+          // planes kernel: there the staging code pushed the registers into spills, measured 2.5%
+          // slower.)
+          static_assert(kPfThreads / kWave * 2048 <= kSxStageMax, "epilogue staging: 2 KB per wave");
+          __builtin_amdgcn_s_barrier();
+          uint8_t* ob = ((nk - 1) % 3 == 0 ? sx_stage<0>() : ((nk - 1) % 3 == 1 ? sx_stage<1>() : sx_stage<2>())) + wv * 2048;
+          pf_epilogue_staged<NMAT>(p, T, acc, wglob, wn, li, lg, ob);
+        } else {
+          pf_epilogue<NMAT>(p, T, acc, wglob, 0, wn, li, lg);
+        }
+      } else {
+        sx_epilogue<NMAT>(p, T, acc, wn, li, lg);
+      }
+    };
+    const int rb = (T.mrows + 15) >> 4;                              // workgroup-uniform
+    if (rb >= 4) run(std::integral_constant<int, 4>());
+    else if (rb == 3) run(std::integral_constant<int, 3>());
+    else if (rb == 2) run(std::integral_constant<int, 2>());
+    else run(std::integral_constant<int, 1>());
   }
   // the last tile leaves its unread repeat loads in flight: let them land
   // before the workgroup's LDS is released
