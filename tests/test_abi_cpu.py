@@ -34,6 +34,18 @@ def test_every_declared_function_is_exported():
     assert set(moe.EXPORTS) == set(names)
 
 
+def test_every_kernel_launch_stub_is_defined():
+    """A kernel template whose host-side instantiation the compiler drops leaves
+    its launch stub undefined; the library then fails to load on use."""
+    import shutil
+    import subprocess
+    if shutil.which("nm") is None:
+        pytest.skip("nm not available")
+    undef = subprocess.run(["nm", "-u", moe.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    stubs = [l.split()[-1] for l in undef.splitlines() if "__device_stub__" in l]
+    assert not stubs, stubs[:4]
+
+
 def _err(status, expect):
     assert status == expect, (status, moe.lib.moe_last_error())
     assert moe.lib.moe_last_error()
