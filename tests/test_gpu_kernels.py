@@ -129,7 +129,8 @@ def test_permute_parity(T, E, invalid):
 # --------------------------------------------------------- route + permute
 @pytest.mark.parametrize("T,E,n_group,topk_group,top_k,with_bias", [
     (0, 256, 8, 4, 8, False), (1, 256, 8, 4, 8, False), (2, 256, 8, 4, 8, True), (3, 64, 4, 2, 6, False),
-    (4, 256, 8, 4, 16, True), (4, 16, 2, 1, 3, False), (7, 256, 8, 4, 8, True), (64, 256, 8, 4, 8, True),
+    (4, 256, 8, 4, 16, True), (4, 16, 2, 1, 3, False), (7, 256, 8, 4, 8, True), (8, 256, 8, 4, 8, False),
+    (12, 64, 4, 2, 6, True), (16, 256, 8, 4, 16, True), (17, 256, 8, 4, 8, False), (64, 256, 8, 4, 8, True),
     (255, 256, 8, 4, 8, False), (256, 256, 8, 4, 8, False), (300, 256, 8, 4, 8, True), (513, 64, 4, 2, 6, False),
     (64, 16, 2, 1, 3, False)])
 def test_route_permute_parity(T, E, n_group, topk_group, top_k, with_bias):
