@@ -5,7 +5,9 @@
 //
 // A workgroup takes one token and 2048 hidden elements; each thread owns 8
 // consecutive elements (16-byte loads of bf16), so every gathered expert row
-// is read once, coalesced.
+// is read once, coalesced.  Expert rows and the residual are read with the
+// non-temporal cache policy: nothing reads them again (prefill layer 0.7%
+// faster).
 #include "common.h"
 
 namespace moe {
@@ -27,7 +29,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const uint16_t* _
   const int kk = TK > 0 ? TK : top_k;
   float acc[8];
   if (resid) {
-    const u32x4 v = *(const u32x4*)(resid + t * h + c);
+    const u32x4 v = __builtin_nontemporal_load((const u32x4*)(resid + t * h + c));
 #pragma unroll
     for (int i = 0; i < 4; ++i) { acc[2 * i] = bf16_lo(v[i]); acc[2 * i + 1] = bf16_hi(v[i]); }
   } else {
@@ -47,7 +49,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const uint16_t* _
 #pragma unroll
     for (int j = 0; j < TK; ++j) {
       r[j] = slot_rows[t * TK + j];                                  // uniform: scalar loads
-      v[j] = *(const u32x4*)(eo + (int64_t)max(r[j], 0) * h + c);
+      v[j] = __builtin_nontemporal_load((const u32x4*)(eo + (int64_t)max(r[j], 0) * h + c));
     }
 #pragma unroll
     for (int j = 0; j < TK; ++j)
