@@ -196,31 +196,6 @@ __device__ __forceinline__ uint32_t e2m1_code(float ax, float s) {
   return c;
 }
 
-// Quantise 16 floats (exact bf16 values) with global scale g (power of two).
-// Writes 8 code bytes (as two dwords) and returns the E4M3 scale byte.
-__device__ __forceinline__ uint32_t quant16(const float* x, float inv_g, uint32_t& lo, uint32_t& hi) {
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
-  // s = E4M3(amax / (6 g)): amax * inv_g is exact, the division is correctly rounded
-  float target = (amax * inv_g) / 6.0f;
-  uint32_t sb = f32_to_e4m3_sat(target);
-  float s = e4m3_to_f32(sb);
-  uint32_t w[2] = {0u, 0u};
-  if (s > 0.0f) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float xs = x[i] * inv_g;                        // exact
-      uint32_t c = e2m1_code(fabsf(xs), s);
-      uint32_t nib = c | ((__float_as_uint(xs) >> 28) & 8u);   // sign of x
-      w[i >> 3] |= nib << (4 * (i & 7));
-    }
-  }
-  lo = w[0];
-  hi = w[1];
-  return sb;
-}
-
 // ------------------------------------------------------------- MXFP8
 // floor(log2 a) for a finite float a > 0, normal or subnormal
 __device__ __forceinline__ int floor_log2_f32(float a) {
