@@ -39,8 +39,9 @@ MXC_BYTES_PER_WEIGHT = 0.5 + 0.5 / 32.0       # compact MXFP4: a 4-bit exponent 
 # HBM bytes per launch of the decode gate/up GEMM at 64 tokens, measured with
 # rocprofv3 --pmc (FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000, the factors a plain
 # 1 GiB device copy gives), keyed by the hash of the kernel's sources at the
-# time; a changed kernel has no entry and reports null.
-MEASURED_TRAFFIC = {"6c07dd1792f9b8b4": 2019543159}
+# time and the token count; a changed kernel or another batch has no entry and
+# reports null.
+MEASURED_TRAFFIC = {("6c07dd1792f9b8b4", 64): 2019543159}
 
 
 def log(*a):
@@ -269,7 +270,7 @@ def main():
     achieved = gu_bytes / (main_r["gate_up_ms"] / 1e3) / 1e9
     lb = layer_bytes(main_r["D"], T, s)
     src_hash = kernel_source_hash()   # of the decode kernel
-    tr = MEASURED_TRAFFIC.get(src_hash)
+    tr = MEASURED_TRAFFIC.get((src_hash, T))
     out = {
         "metric": "MoE-layer tokens/s at 1 MI355X (decode shape, HBM roofline)",
         "value": round(tok_s, 1),

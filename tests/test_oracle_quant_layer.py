@@ -8,6 +8,7 @@ import torch
 from scipy.special import expit
 
 import oracle
+from oracle.layer import down_proj
 from synth import WORKLOADS, activations, bf16_bits_from_f32, expert_weights, logits as gen_logits, random_bf16
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
@@ -345,3 +346,53 @@ def test_saliency_equal_outputs_closed_form():
     for e in range(E - 1):
         np.testing.assert_allclose(S[e], g[ids == e].mean() * np.linalg.norm(v), rtol=1e-13)
     assert np.isnan(S[E - 1])
+
+
+def test_down_proj_against_exact_rationals():
+    """down_proj contracts z [m, I] with W_down [H, I] over I (o = z W_downᵀ, the
+    outer W_down of the REAP saliency equation): each float64 output lies within
+    the float64 summation bound of the exact rational sum of its terms, and an
+    operand transposed or a term dropped fails the check."""
+    w = WORKLOADS["tiny"]
+    W = expert_weights(w)
+    table = _e2m1_table()
+    z = random_bf16(41, (3, w.shape.inter), std=0.5)
+    zs = oracle.bf16_value(z)
+    I = w.shape.inter
+    for e in (0, 13, 31):
+        wd = oracle.dequant_mx(W["down"][0][e], W["down"][1][e])
+        assert wd.shape == (w.shape.hidden, I)
+        got = down_proj(z, wd)
+        assert got.shape == (3, w.shape.hidden)
+        for t in range(3):
+            zf = [Fraction(float(v)) for v in zs[t]]
+            for n in range(0, w.shape.hidden, 29):
+                acc, mag = Fraction(0), Fraction(0)
+                for k in range(I):
+                    byte = int(W["down"][0][e, n, k // 2])
+                    nib = (byte & 0xF) if k % 2 == 0 else byte >> 4
+                    val = Fraction(table[nib & 7]) * (-1 if nib & 8 else 1) * \
+                        Fraction(2) ** (int(W["down"][1][e, n, k // 32]) - 127)
+                    acc += val * zf[k]
+                    mag += abs(val * zf[k])
+                assert abs(Fraction(float(got[t, n])) - acc) <= I * Fraction(2) ** -53 * mag
+
+
+def test_down_proj_nvfp4_on_exactly_representable_z():
+    """A z whose every 16-value block is E2M1 values times one power of two the
+    E4M3 scale can hold is quantised to NVFP4 without loss, so the W4A4 down
+    projection equals the bf16 one on it; the same z perturbed by one bf16 ulp
+    in one element is not representable and the results differ."""
+    rng = np.random.default_rng(43)
+    table = np.array(_e2m1_table())
+    I, H = 64, 48
+    mags = table[rng.integers(0, 8, (2, I))] * np.where(rng.random((2, I)) < 0.5, -1.0, 1.0)
+    mags[:, ::16] = 6.0                        # every block reaches the E2M1 maximum
+    scale = 2.0 ** rng.integers(-4, 4, (2, I // 16)).repeat(16, axis=1)
+    z = bf16_bits_from_f32((mags * scale).astype(np.float32))
+    wd = rng.standard_normal((H, I))
+    ref = down_proj(z, wd)
+    np.testing.assert_array_equal(down_proj(z, wd, act_mode="nvfp4"), ref)
+    z2 = z.copy()
+    z2[0, 5] = np.uint16(int(z2[0, 5]) + 1) if mags[0, 5] != 0 else np.uint16(0x3F81)
+    assert not np.array_equal(down_proj(z2, wd, act_mode="nvfp4"), down_proj(z2, wd))
