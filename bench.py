@@ -34,6 +34,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP4_PEAK_TFLOPS = 10100.0      # MI355X dense fp4 MFMA
 MX_BYTES_PER_WEIGHT = 0.5 + 1.0 / 32.0
+HOST_LEAD_CYCLES = 40_000_000  # GPU spin before a timed eager loop: ~20 ms at 2 GHz, time to queue its steps
 MXC_BYTES_PER_WEIGHT = 0.5 + 0.5 / 32.0       # compact MXFP4: a 4-bit exponent code per 32 weights
 
 # HBM bytes per launch of the decode gate/up GEMM at 64 tokens, measured with
@@ -90,7 +91,10 @@ def time_steps(layers, inputs, steps, warmup, algo=0, ev_names=("gate_up", "down
     """Run warmup + timed steps, rotating over (layer, input) pairs.  Returns
     (ms per step, {kernel: mean launch ms over the timed steps}); the launch
     times come from HIP events recorded on the launching stream around the
-    gate/up and down GEMM launches."""
+    gate/up and down GEMM launches.  The timed steps start behind a short GPU
+    spin, so the host has queued them before the GPU reaches them and the
+    events time the kernels, not the host's launch gaps (which dominate a
+    1-token step)."""
     import torch
     n = len(layers)
     for i in range(warmup):
@@ -101,6 +105,7 @@ def time_steps(layers, inputs, steps, warmup, algo=0, ev_names=("gate_up", "down
           for k in ev_names}
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    torch.cuda._sleep(HOST_LEAD_CYCLES)
     start.record()
     for i in range(steps):
         x, l, b, r = inputs[i % len(inputs)]
